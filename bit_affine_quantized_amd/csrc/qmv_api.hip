@@ -1,0 +1,343 @@
+// C ABI of libqmv.so (declared in include/qmv.h): host-side validation,
+// kernel selection and launch.  Validation happens before any HIP call, so
+// every argument error is reported without touching a device.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "qmv.h"
+#include "pack_kernels.h"
+#include "qmv_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return QMV_OK;
+}
+
+int check_launch(const char *what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(QMV_EHIP, "%s: HIP launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+constexpr int64_t kMaxLds = 160 * 1024;   // gfx950 LDS per workgroup
+
+bool bits_ok(int bits) {
+  return bits == 2 || bits == 3 || bits == 4 || bits == 5 || bits == 6 || bits == 8;
+}
+bool group_ok(int g) { return g == 32 || g == 64 || g == 128; }
+int gshift_of(int g) { return g == 32 ? 0 : g == 64 ? 1 : 2; }
+
+// Shape rules shared by every product (mlx/ops.cpp, extract_quantized_matmul_dims:
+// w is uint32 with K*bits/32 words per row and K/group_size scales per row).
+int check_common(const char *fn, int64_t N, int64_t K, int group_size, int bits) {
+  if (!bits_ok(bits)) return fail(QMV_EINVAL, "%s: bits=%d not in {2,3,4,5,6,8}", fn, bits);
+  if (!group_ok(group_size))
+    return fail(QMV_EINVAL, "%s: group_size=%d not in {32,64,128}", fn, group_size);
+  if (N <= 0 || K <= 0) return fail(QMV_EINVAL, "%s: N=%lld and K=%lld must be positive", fn,
+                                    (long long)N, (long long)K);
+  if (K % group_size != 0)
+    return fail(QMV_EINVAL, "%s: K=%lld is not a multiple of group_size=%d", fn, (long long)K,
+                group_size);
+  if (K > (int64_t(1) << 30) || N > (int64_t(1) << 40))
+    return fail(QMV_EINVAL, "%s: K=%lld or N=%lld too large", fn, (long long)K, (long long)N);
+  return QMV_OK;
+}
+
+// The kernels read x (and gate/up) and packed rows with 16-byte vector loads.
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_aligned(const char *fn, const void *p, const char *name) {
+  if (!aligned16(p)) return fail(QMV_EINVAL, "%s: %s must be 16-byte aligned", fn, name);
+  return QMV_OK;
+}
+
+template <typename Kern>
+void allow_lds(Kern kern, int64_t bytes) {
+  if (bytes > 64 * 1024)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
+}
+
+// ------------------------------------------------------------------ qmv family
+#ifndef QMV_RPW
+#define QMV_RPW 4
+#endif
+constexpr int kRpw = QMV_RPW;
+
+template <int BITS, int MV, int XIN>
+int launch_qmv_t(const qmvk::QmvArgs &a, hipStream_t st) {
+  constexpr bool PAIR = (BITS <= 6) && (XIN == qmvk::XIN_PLAIN);
+  const int64_t Kc = a.K / 32;
+  const int64_t lds = (XIN == qmvk::XIN_SILU ? 1 : MV) * Kc * qmvk::stage_bytes_per_chunk<PAIR>();
+  const int64_t rows = static_cast<int64_t>(a.nmat) * a.N;
+  const int64_t rows_per_block = qmvk::kWavesPerBlock * kRpw;
+  const int64_t blocks = (rows + rows_per_block - 1) / rows_per_block;
+  if (blocks > 0x7FFFFFFF) return fail(QMV_EUNSUPPORTED, "qmv: too many rows");
+  auto kern = qmvk::qmv_kernel<BITS, kRpw, MV, XIN>;
+  allow_lds(kern, lds);
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(qmvk::kBlock),
+                     static_cast<size_t>(lds), st, a);
+  return check_launch("qmv");
+}
+
+template <int MV, int XIN>
+int launch_qmv_bits(int bits, const qmvk::QmvArgs &a, hipStream_t st) {
+  switch (bits) {
+    case 2: return launch_qmv_t<2, MV, XIN>(a, st);
+    case 3: return launch_qmv_t<3, MV, XIN>(a, st);
+    case 4: return launch_qmv_t<4, MV, XIN>(a, st);
+    case 5: return launch_qmv_t<5, MV, XIN>(a, st);
+    case 6: return launch_qmv_t<6, MV, XIN>(a, st);
+    case 8: return launch_qmv_t<8, MV, XIN>(a, st);
+  }
+  return fail(QMV_EINVAL, "bits=%d", bits);
+}
+
+int64_t qmv_lds_bytes(int bits, int mv, int64_t K) {
+  const bool pair = bits <= 6;
+  return mv * (K / 32) * (pair ? 68 : 132);
+}
+
+// ------------------------------------------------------------------ gather
+constexpr int kGatherRpw = 4;
+constexpr int kGatherMv = 8;
+
+template <int BITS>
+int launch_gather_t(const qmvk::GatherArgs &a0, int64_t E, hipStream_t st) {
+  qmvk::GatherArgs a = a0;
+  const int64_t Kc = a.K / 32;
+  const int64_t lds = kGatherMv * Kc * qmvk::stage_bytes_per_chunk<(BITS <= 6)>();
+  const int64_t rows_per_block = qmvk::kWavesPerBlock * kGatherRpw;
+  const int64_t tiles = (a.N + rows_per_block - 1) / rows_per_block;
+  if (E * tiles > 0x7FFFFFFF) return fail(QMV_EUNSUPPORTED, "gather_qmv: grid too large");
+  a.tiles = static_cast<int>(tiles);
+  auto kern = qmvk::gather_kernel<BITS, kGatherRpw, kGatherMv>;
+  allow_lds(kern, lds);
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(E * tiles)), dim3(qmvk::kBlock),
+                     static_cast<size_t>(lds), st, a);
+  return check_launch("gather_qmv");
+}
+
+template <int BITS>
+int launch_unpack_t(const uint32_t *w_q, int64_t N, int64_t K, uint8_t *codes, hipStream_t st) {
+  const int64_t items = N * (K / 32);
+  const int64_t blocks = (items + 255) / 256;
+  if (blocks > 0x7FFFFFFF) return fail(QMV_EUNSUPPORTED, "qmv_unpack_codes: too large");
+  hipLaunchKernelGGL(qmvk::unpack_kernel<BITS>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                     st, w_q, N, K, codes);
+  return check_launch("qmv_unpack_codes");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *qmv_last_error(void) { return g_last_error.c_str(); }
+
+int qmv_pack(const float *w, int64_t N, int64_t K, int group_size, int bits, uint32_t *w_q,
+             uint16_t *scales, uint16_t *biases, void *stream) {
+  if (int rc = check_common("qmv_pack", N, K, group_size, bits)) return rc;
+  if (!w || !w_q || !scales || !biases) return fail(QMV_EINVAL, "qmv_pack: null pointer argument");
+  const int64_t groups = N * (K / group_size);
+  const int64_t blocks = (groups + 255) / 256;
+  if (blocks > 0x7FFFFFFF) return fail(QMV_EUNSUPPORTED, "qmv_pack: too large");
+  hipLaunchKernelGGL(qmvk::pack_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), w, N, K, group_size, bits, w_q, scales,
+                     biases);
+  return check_launch("qmv_pack");
+}
+
+int qmv_unpack_codes(const uint32_t *w_q, int64_t N, int64_t K, int bits, uint8_t *codes,
+                     void *stream) {
+  if (!bits_ok(bits)) return fail(QMV_EINVAL, "qmv_unpack_codes: bits=%d not in {2,3,4,5,6,8}", bits);
+  if (N <= 0 || K <= 0 || K % 32 != 0)
+    return fail(QMV_EINVAL, "qmv_unpack_codes: need N > 0 and K a positive multiple of 32");
+  if (!w_q || !codes) return fail(QMV_EINVAL, "qmv_unpack_codes: null pointer argument");
+  if (int rc = check_aligned("qmv_unpack_codes", w_q, "w_q")) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  switch (bits) {
+    case 2: return launch_unpack_t<2>(w_q, N, K, codes, st);
+    case 3: return launch_unpack_t<3>(w_q, N, K, codes, st);
+    case 4: return launch_unpack_t<4>(w_q, N, K, codes, st);
+    case 5: return launch_unpack_t<5>(w_q, N, K, codes, st);
+    case 6: return launch_unpack_t<6>(w_q, N, K, codes, st);
+    default: return launch_unpack_t<8>(w_q, N, K, codes, st);
+  }
+}
+
+int qmv(const uint16_t *x, const uint32_t *w_q, const uint16_t *scales, const uint16_t *biases,
+        void *y, int64_t M, int64_t N, int64_t K, int group_size, int bits, int transpose,
+        int out_dtype, void *stream) {
+  if (int rc = check_common("qmv", N, K, group_size, bits)) return rc;
+  if (M <= 0) return fail(QMV_EINVAL, "qmv: M=%lld must be positive", (long long)M);
+  if (!x || !w_q || !scales || !biases || !y) return fail(QMV_EINVAL, "qmv: null pointer argument");
+  if (out_dtype != QMV_OUT_BF16 && out_dtype != QMV_OUT_F32)
+    return fail(QMV_EINVAL, "qmv: out_dtype=%d unknown", out_dtype);
+  if (transpose != 1)
+    return fail(QMV_EUNSUPPORTED, "qmv: transpose=0 (x @ W with W packed [K,N]) is not implemented");
+  if (int rc = check_aligned("qmv", x, "x")) return rc;
+  if (int rc = check_aligned("qmv", w_q, "w_q")) return rc;
+  const int mv_max = qmv_lds_bytes(bits, 4, K) <= kMaxLds ? 4
+                   : qmv_lds_bytes(bits, 2, K) <= kMaxLds ? 2
+                   : qmv_lds_bytes(bits, 1, K) <= kMaxLds ? 1 : 0;
+  if (mv_max == 0)
+    return fail(QMV_EUNSUPPORTED, "qmv: K=%lld too large for one workgroup's staged x", (long long)K);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const size_t esz = out_dtype == QMV_OUT_F32 ? 4 : 2;
+  for (int64_t m0 = 0; m0 < M; m0 += mv_max) {
+    const int mv = static_cast<int>(M - m0 < mv_max ? M - m0 : mv_max);
+    qmvk::QmvArgs a{};
+    a.x = x + m0 * K;
+    a.mat0 = {w_q, scales, biases, static_cast<char *>(y) + m0 * N * esz};
+    a.mat1 = a.mat0;
+    a.nmat = 1;
+    a.N = N;
+    a.K = static_cast<int>(K);
+    a.M = mv;
+    a.gshift = gshift_of(group_size);
+    a.out_f32 = out_dtype == QMV_OUT_F32;
+    a.y_ld = N;
+    int rc;
+    if (mv == 1) rc = launch_qmv_bits<1, qmvk::XIN_PLAIN>(bits, a, st);
+    else if (mv == 2) rc = launch_qmv_bits<2, qmvk::XIN_PLAIN>(bits, a, st);
+    else rc = launch_qmv_bits<4, qmvk::XIN_PLAIN>(bits, a, st);
+    if (rc) return rc;
+  }
+  return ok();
+}
+
+int qmv_gate_up(const uint16_t *x, const uint32_t *wg, const uint16_t *sg, const uint16_t *bg,
+                const uint32_t *wu, const uint16_t *su, const uint16_t *bu, uint16_t *gate_y,
+                uint16_t *up_y, int64_t N, int64_t K, int group_size, int bits, void *stream) {
+  if (int rc = check_common("qmv_gate_up", N, K, group_size, bits)) return rc;
+  if (!x || !wg || !sg || !bg || !wu || !su || !bu || !gate_y || !up_y)
+    return fail(QMV_EINVAL, "qmv_gate_up: null pointer argument");
+  if (int rc = check_aligned("qmv_gate_up", x, "x")) return rc;
+  if (int rc = check_aligned("qmv_gate_up", wg, "wg")) return rc;
+  if (int rc = check_aligned("qmv_gate_up", wu, "wu")) return rc;
+  if (qmv_lds_bytes(bits, 1, K) > kMaxLds)
+    return fail(QMV_EUNSUPPORTED, "qmv_gate_up: K=%lld too large", (long long)K);
+  qmvk::QmvArgs a{};
+  a.x = x;
+  a.mat0 = {wg, sg, bg, gate_y};
+  a.mat1 = {wu, su, bu, up_y};
+  a.nmat = 2;
+  a.N = N;
+  a.K = static_cast<int>(K);
+  a.M = 1;
+  a.gshift = gshift_of(group_size);
+  a.out_f32 = 0;
+  a.y_ld = N;
+  const int rc = launch_qmv_bits<1, qmvk::XIN_PLAIN>(bits, a, static_cast<hipStream_t>(stream));
+  return rc ? rc : ok();
+}
+
+int qmv_silu_gate_resid(const uint16_t *gate, const uint16_t *up, const uint16_t *x_resid,
+                        const uint32_t *w_q, const uint16_t *scales, const uint16_t *biases,
+                        void *y, int64_t N, int64_t K, int group_size, int bits, int out_dtype,
+                        void *stream) {
+  if (int rc = check_common("qmv_silu_gate_resid", N, K, group_size, bits)) return rc;
+  if (!gate || !up || !w_q || !scales || !biases || !y)
+    return fail(QMV_EINVAL, "qmv_silu_gate_resid: null pointer argument");
+  if (out_dtype != QMV_OUT_BF16 && out_dtype != QMV_OUT_F32)
+    return fail(QMV_EINVAL, "qmv_silu_gate_resid: out_dtype=%d unknown", out_dtype);
+  if (int rc = check_aligned("qmv_silu_gate_resid", gate, "gate")) return rc;
+  if (int rc = check_aligned("qmv_silu_gate_resid", up, "up")) return rc;
+  if (int rc = check_aligned("qmv_silu_gate_resid", w_q, "w_q")) return rc;
+  if ((K / 32) * 132 > kMaxLds)
+    return fail(QMV_EUNSUPPORTED, "qmv_silu_gate_resid: K=%lld too large", (long long)K);
+  qmvk::QmvArgs a{};
+  a.x = gate;
+  a.up = up;
+  a.xres = x_resid;
+  a.mat0 = {w_q, scales, biases, y};
+  a.mat1 = a.mat0;
+  a.nmat = 1;
+  a.N = N;
+  a.K = static_cast<int>(K);
+  a.M = 1;
+  a.gshift = gshift_of(group_size);
+  a.out_f32 = out_dtype == QMV_OUT_F32;
+  a.y_ld = N;
+  const int rc = launch_qmv_bits<1, qmvk::XIN_SILU>(bits, a, static_cast<hipStream_t>(stream));
+  return rc ? rc : ok();
+}
+
+int gather_qmv(const uint16_t *x, int64_t Bx, const uint32_t *w_q, const uint16_t *scales,
+               const uint16_t *biases, int64_t E, const uint32_t *lhs_indices,
+               const uint32_t *rhs_indices, int64_t P, void *y, int64_t M, int64_t N, int64_t K,
+               int group_size, int bits, int transpose, int sorted_indices, int out_dtype,
+               void *stream) {
+  if (int rc = check_common("gather_qmv", N, K, group_size, bits)) return rc;
+  if (!x || !w_q || !scales || !biases || !y) return fail(QMV_EINVAL, "gather_qmv: null pointer argument");
+  if (M <= 0 || Bx <= 0 || E <= 0)
+    return fail(QMV_EINVAL, "gather_qmv: M=%lld, Bx=%lld, E=%lld must be positive", (long long)M,
+                (long long)Bx, (long long)E);
+  if (out_dtype != QMV_OUT_BF16 && out_dtype != QMV_OUT_F32)
+    return fail(QMV_EINVAL, "gather_qmv: out_dtype=%d unknown", out_dtype);
+  if ((lhs_indices == nullptr) != (rhs_indices == nullptr))
+    return fail(QMV_EINVAL, "gather_qmv: lhs_indices and rhs_indices must both be given or both NULL");
+  if (transpose != 1)
+    return fail(QMV_EUNSUPPORTED, "gather_qmv: transpose=0 is not implemented");
+  if (!lhs_indices) {
+    // no indices: the plain quantized product of x[0] with W[0]
+    const int rc = qmv(x, w_q, scales, biases, y, M, N, K, group_size, bits, 1, out_dtype, stream);
+    return rc;
+  }
+  if (P <= 0) return fail(QMV_EINVAL, "gather_qmv: P=%lld must be positive", (long long)P);
+  if (int rc = check_aligned("gather_qmv", x, "x")) return rc;
+  if (int rc = check_aligned("gather_qmv", w_q, "w_q")) return rc;
+  if (!sorted_indices && P > qmvk::kGatherListMax)
+    return fail(QMV_EUNSUPPORTED,
+                "gather_qmv: unsorted indices with P=%lld > %d pairs; pass rhs sorted (sorted_indices=1)",
+                (long long)P, qmvk::kGatherListMax);
+  if (qmv_lds_bytes(bits, kGatherMv, K) > kMaxLds)
+    return fail(QMV_EUNSUPPORTED, "gather_qmv: K=%lld too large", (long long)K);
+  if (M > (int64_t(1) << 20) || P > (int64_t(1) << 30))
+    return fail(QMV_EUNSUPPORTED, "gather_qmv: M or P too large");
+  qmvk::GatherArgs a{};
+  a.x = x;
+  a.w = w_q;
+  a.s = scales;
+  a.b = biases;
+  a.lhs = lhs_indices;
+  a.rhs = rhs_indices;
+  a.P = P;
+  a.N = N;
+  a.K = static_cast<int>(K);
+  a.M = static_cast<int>(M);
+  a.gshift = gshift_of(group_size);
+  a.sorted = sorted_indices ? 1 : 0;
+  a.out_f32 = out_dtype == QMV_OUT_F32;
+  a.y = y;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int rc;
+  switch (bits) {
+    case 2: rc = launch_gather_t<2>(a, E, st); break;
+    case 3: rc = launch_gather_t<3>(a, E, st); break;
+    case 4: rc = launch_gather_t<4>(a, E, st); break;
+    case 5: rc = launch_gather_t<5>(a, E, st); break;
+    case 6: rc = launch_gather_t<6>(a, E, st); break;
+    default: rc = launch_gather_t<8>(a, E, st); break;
+  }
+  return rc ? rc : ok();
+}
+
+}  // extern "C"

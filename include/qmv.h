@@ -1,0 +1,150 @@
+/*
+ * qmv.h -- C ABI of libqmv.so: affine group-quantized matrix-vector products
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (cited by page and section):
+ *   An [N, K] weight W is stored as b-bit codes q (b in {2,3,4,5,6,8}) plus one
+ *   bf16 scale s and one bf16 bias z per group of `group_size` consecutive
+ *   K-elements of a row; the dequantized weight is w_hat = s*q + z
+ *   (mlx-cpu 0.30.1 quantized.h, affine_dequantize).  The products use
+ *   w_hat exactly; qdot's regrouping y = s*sum(q*x) + z*sum(x) per group is
+ *   the same sum (quantized.h, qdot).
+ *
+ * Layout of a packed weight (quantized.h, affine_quantize / affine_dequantize;
+ * mlx/ops.cpp, extract_quantized_matmul_dims):
+ *   w_q    uint32 [N, K*bits/32], row-major.  Row n is a little-endian bit
+ *          stream: code k occupies bits [bits*k, bits*k + bits), least
+ *          significant bit first; stream bit i is bit (i mod 32) of word
+ *          (i div 32).  For 3-, 5- and 6-bit codes this is the page's
+ *          8-codes-in-3-bytes, 8-in-5 and 4-in-3 byte packs.
+ *   scales, biases   bf16 bit patterns (uint16) [N, K/group_size].
+ *
+ * Conventions for every entry point:
+ *   - All array pointers are DEVICE pointers owned by the caller; the library
+ *     never allocates, frees or keeps them.  bf16 values travel as uint16 bit
+ *     patterns.  `stream` is a hipStream_t (NULL = the legacy default stream).
+ *   - Calls are asynchronous on `stream`: they enqueue kernels and return.
+ *     Results are visible after the stream is synchronized.
+ *   - Arguments are validated on the host before any HIP call.  A bad size,
+ *     an unsupported bits/group_size, a null required pointer or K not a
+ *     multiple of group_size returns QMV_EINVAL; a valid request this build
+ *     does not implement returns QMV_EUNSUPPORTED (never a silent slow path,
+ *     as the metrale QuantWeights trait asks of its fused defaults); a HIP
+ *     launch error returns QMV_EHIP.  qmv_last_error() then describes it.
+ *   - bits in {2,3,4,5,6,8}; group_size in {32,64,128}; K % group_size == 0.
+ *   - out_dtype QMV_OUT_BF16 rounds each output once, to nearest even;
+ *     QMV_OUT_F32 writes the fp32 accumulator (a debugging mode).
+ *   - Index arrays are not range-checked on the device (that needs a device
+ *     read); out-of-range indices are undefined behaviour.
+ *   - Concurrent calls on different streams are independent.
+ */
+#ifndef QMV_H
+#define QMV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    QMV_OK = 0,
+    QMV_EINVAL = -1,
+    QMV_EUNSUPPORTED = -2,
+    QMV_EHIP = -3
+};
+
+enum { QMV_OUT_BF16 = 0, QMV_OUT_F32 = 1 };
+
+/*
+ * qmv_pack -- quantize and pack an fp32 weight on the device
+ * (quantized.h, affine_quantize).  Per group, in IEEE fp32 with correctly
+ * rounded division and round-half-away-from-zero:
+ *   w_min = min(FLT_MAX, min w), w_max = max(0, max w),
+ *   s = max((w_max - w_min)/(2^bits - 1), 1e-7), negated unless
+ *   |w_min| > |w_max|; edge = that endpoint; q0 = round(edge/s);
+ *   if q0 != 0 then s = edge/q0, z = edge, else z = 0;
+ *   q = min(round((w - z)/s), 2^bits - 1);  s and z are stored as bf16
+ *   (nearest even), the codes use the fp32 values.
+ * w: fp32 [N, K].  Outputs: w_q [N, K*bits/32], scales/biases [N, K/group_size].
+ */
+int qmv_pack(const float *w, int64_t N, int64_t K, int group_size, int bits,
+             uint32_t *w_q, uint16_t *scales, uint16_t *biases, void *stream);
+
+/*
+ * qmv -- quantized matmul at decode batch sizes (mlx/ops.cpp quantized_matmul;
+ * quantized.h qmv_fast / qmv kernels).
+ *   transpose = 1: W packed [N, K]; y[m, n] = sum_k x[m, k] * w_hat[n, k].
+ *   transpose = 0: W packed [K, N] (groups along N); y = x @ w_hat.
+ *                  Not implemented in this build: returns QMV_EUNSUPPORTED.
+ * x: bf16 [M, K].  y: [M, N], bf16 or fp32 per out_dtype.  M >= 1 (the W
+ * stream is read once per slab of up to 4 rows of x).
+ */
+int qmv(const uint16_t *x, const uint32_t *w_q, const uint16_t *scales,
+        const uint16_t *biases, void *y, int64_t M, int64_t N, int64_t K,
+        int group_size, int bits, int transpose, int out_dtype, void *stream);
+
+/*
+ * qmv_gate_up -- dual-output matvec over one input in ONE launch
+ * (metrale QuantWeights::gemv_gate_up_with, whose default is two gemv calls;
+ * the MlxInt8Weight implementation uses a single launch).
+ *   gate_y[n] = sum_k w_hat_g[n, k] x[k],  up_y[n] = sum_k w_hat_u[n, k] x[k]
+ * x: bf16 [K]; both weights [N, K] with the same bits and group_size;
+ * gate_y, up_y: bf16 [N].  Results equal two qmv calls bit for bit.
+ */
+int qmv_gate_up(const uint16_t *x,
+                const uint32_t *wg, const uint16_t *sg, const uint16_t *bg,
+                const uint32_t *wu, const uint16_t *su, const uint16_t *bu,
+                uint16_t *gate_y, uint16_t *up_y, int64_t N, int64_t K,
+                int group_size, int bits, void *stream);
+
+/*
+ * qmv_silu_gate_resid -- fused FFN tail (metrale QuantWeights::
+ * gemv_silu_gate_resid and gemv_silu_gate):
+ *   y[n] = x_resid[n] + sum_k w_hat[n, k] * silu(gate[k]) * up[k],
+ *   silu(v) = v / (1 + exp(-v)).
+ * gate, up: bf16 [K]; x_resid: bf16 [N] or NULL (then no residual add);
+ * W: [N, K]; y: [N] bf16 or fp32.  silu(gate)*up is formed in fp32 and not
+ * rounded; the residual is added in fp32 before the single output rounding.
+ */
+int qmv_silu_gate_resid(const uint16_t *gate, const uint16_t *up,
+                        const uint16_t *x_resid, const uint32_t *w_q,
+                        const uint16_t *scales, const uint16_t *biases,
+                        void *y, int64_t N, int64_t K, int group_size,
+                        int bits, int out_dtype, void *stream);
+
+/*
+ * gather_qmv -- expert-gathered matvec (mlx.core.gather_qmm; quantized.h
+ * adjust_matrix_offsets for the gather kernels):
+ *   for p in [0, P):  y[p] (M x N) = x[lhs[p]] (M x K) @ w_hat[rhs[p]]^T
+ * x: bf16 [Bx, M, K];  w_q: [E, N, K*bits/32];  scales/biases: [E, N, K/g];
+ * lhs_indices, rhs_indices: uint32 [P] (flat batch indices);  y: [P, M, N].
+ * Both index arrays NULL: identical to qmv on x[0] and W[0] (mlx/ops.cpp
+ * gather_qmm without indices is quantized_matmul); then P is ignored and y is
+ * [M, N].  Exactly one NULL is QMV_EINVAL.  sorted_indices = 1 promises rhs is
+ * non-decreasing; it may make the call faster and never changes the results
+ * (every output is computed with the same arithmetic either way).
+ * transpose must be 1 (else QMV_EUNSUPPORTED).
+ */
+int gather_qmv(const uint16_t *x, int64_t Bx, const uint32_t *w_q,
+               const uint16_t *scales, const uint16_t *biases, int64_t E,
+               const uint32_t *lhs_indices, const uint32_t *rhs_indices,
+               int64_t P, void *y, int64_t M, int64_t N, int64_t K,
+               int group_size, int bits, int transpose, int sorted_indices,
+               int out_dtype, void *stream);
+
+/*
+ * qmv_unpack_codes -- debugging export: runs the qmv kernels' own in-register
+ * unpacking on w_q [N, K*bits/32] and writes one code per byte, codes [N, K].
+ */
+int qmv_unpack_codes(const uint32_t *w_q, int64_t N, int64_t K, int bits,
+                     uint8_t *codes, void *stream);
+
+/* Message for the last non-QMV_OK return on the calling thread ("" if none). */
+const char *qmv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMV_H */

@@ -1,0 +1,123 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/qmv.h declares, and rejects bad arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_affine_quantized_amd as q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qmv.h")
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation runs first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:int|const char\s*\*)\s*(\w+)\s*\(", text, re.M)
+
+
+def test_header_declares_the_boundary():
+    names = set(declared_functions())
+    assert {"qmv_pack", "qmv", "qmv_gate_up", "qmv_silu_gate_resid",
+            "gather_qmv", "qmv_unpack_codes", "qmv_last_error"} <= names
+
+
+def test_library_exports_every_declared_symbol():
+    L = q.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert set(declared_functions()) - {"qmv_last_error"} == set(q.SIGNATURES)
+
+
+def _qmv(**kw):
+    a = dict(x=FAKE, w=FAKE, s=FAKE, b=FAKE, y=FAKE, M=1, N=16, K=64, g=64,
+             bits=4, transpose=1, out=0)
+    a.update(kw)
+    return q.lib().qmv(a["x"], a["w"], a["s"], a["b"], a["y"], a["M"], a["N"],
+                       a["K"], a["g"], a["bits"], a["transpose"], a["out"],
+                       None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(bits=7), q.QMV_EINVAL, "bits=7"),
+    (dict(bits=1), q.QMV_EINVAL, "bits=1"),
+    (dict(g=48, K=96), q.QMV_EINVAL, "group_size=48"),
+    (dict(g=16, K=64), q.QMV_EINVAL, "group_size=16"),
+    (dict(K=96), q.QMV_EINVAL, "not a multiple"),
+    (dict(N=0), q.QMV_EINVAL, "positive"),
+    (dict(K=0), q.QMV_EINVAL, "positive"),
+    (dict(M=0), q.QMV_EINVAL, "M=0"),
+    (dict(x=None), q.QMV_EINVAL, "null"),
+    (dict(w=None), q.QMV_EINVAL, "null"),
+    (dict(y=None), q.QMV_EINVAL, "null"),
+    (dict(out=2), q.QMV_EINVAL, "out_dtype"),
+    (dict(transpose=0), q.QMV_EUNSUPPORTED, "transpose=0"),
+    (dict(x=ctypes.c_void_p(0x1002)), q.QMV_EINVAL, "aligned"),
+    (dict(w=ctypes.c_void_p(0x1008)), q.QMV_EINVAL, "aligned"),
+])
+def test_qmv_rejects_bad_arguments(kw, code, msg):
+    assert _qmv(**kw) == code
+    assert msg in q.lib().qmv_last_error().decode()
+
+
+def test_pack_rejects_bad_arguments():
+    L = q.lib()
+    assert L.qmv_pack(FAKE, 4, 64, 64, 7, FAKE, FAKE, FAKE, None) == q.QMV_EINVAL
+    assert L.qmv_pack(None, 4, 64, 64, 4, FAKE, FAKE, FAKE, None) == q.QMV_EINVAL
+    assert L.qmv_pack(FAKE, 4, 100, 64, 4, FAKE, FAKE, FAKE, None) == q.QMV_EINVAL
+
+
+def test_fused_reject_bad_arguments():
+    L = q.lib()
+    assert L.qmv_gate_up(FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE,
+                         16, 64, 64, 4, None) == q.QMV_EINVAL
+    assert L.qmv_silu_gate_resid(FAKE, None, None, FAKE, FAKE, FAKE, FAKE, 16,
+                                 64, 64, 8, 0, None) == q.QMV_EINVAL
+    assert L.qmv_silu_gate_resid(FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 16,
+                                 64, 64, 8, 5, None) == q.QMV_EINVAL
+
+
+def test_gather_rejects_bad_arguments():
+    L = q.lib()
+    base = [FAKE, 1, FAKE, FAKE, FAKE, 4]
+    tail = [FAKE, 1, 16, 64, 64, 4]
+    # exactly one index array
+    assert L.gather_qmv(*base, FAKE, None, 8, *tail, 1, 0, 0, None) == q.QMV_EINVAL
+    assert "both" in L.qmv_last_error().decode()
+    # P must be positive when indices are given
+    assert L.gather_qmv(*base, FAKE, FAKE, 0, *tail, 1, 0, 0, None) == q.QMV_EINVAL
+    # E must be positive
+    assert L.gather_qmv(FAKE, 1, FAKE, FAKE, FAKE, 0, FAKE, FAKE, 8, *tail, 1,
+                        0, 0, None) == q.QMV_EINVAL
+    # transpose=0 not implemented
+    assert L.gather_qmv(*base, FAKE, FAKE, 8, *tail, 0, 0, 0, None) == \
+        q.QMV_EUNSUPPORTED
+    # unsorted beyond the in-kernel list capacity
+    assert L.gather_qmv(*base, FAKE, FAKE, 5000, *tail, 1, 0, 0, None) == \
+        q.QMV_EUNSUPPORTED
+
+
+def test_unpack_rejects_bad_arguments():
+    L = q.lib()
+    assert L.qmv_unpack_codes(FAKE, 4, 48, 4, FAKE, None) == q.QMV_EINVAL
+    assert L.qmv_unpack_codes(FAKE, 4, 64, 7, FAKE, None) == q.QMV_EINVAL
+    assert L.qmv_unpack_codes(None, 4, 64, 4, FAKE, None) == q.QMV_EINVAL
+
+
+def test_error_message_clears_on_success_path_is_thread_local():
+    import threading
+    L = q.lib()
+    _qmv(bits=7)
+    seen = {}
+
+    def other():
+        seen["msg"] = L.qmv_last_error().decode()
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen["msg"] == ""
+    assert "bits=7" in L.qmv_last_error().decode()
