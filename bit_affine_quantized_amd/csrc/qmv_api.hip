@@ -77,7 +77,7 @@ void allow_lds(Kern kern, int64_t bytes) {
 
 // ------------------------------------------------------------------ qmv family
 #ifndef QMV_RPW
-#define QMV_RPW 4
+#define QMV_RPW 2
 #endif
 constexpr int kRpw = QMV_RPW;
 

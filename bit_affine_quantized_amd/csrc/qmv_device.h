@@ -10,14 +10,14 @@
 //
 //  * bf16 pair path (b <= 6).  Each code q is written into the top b bits of
 //    the 7-bit mantissa of a bf16 whose exponent is fixed at 2^7:
-//        value = 128 + q * 2^P,   P = 7 - b   (exact, 128 + q*2^P <= 255)
-//    Two such values share a dword and meet a dword of two x values that were
-//    staged pre-multiplied by 2^-P, so one v_dot2c_f32_bf16 adds
-//        (2^b + q_lo) * x_lo + (2^b + q_hi) * x_hi
-//    into an fp32 accumulator.  Over a chunk that is D = sum(q*x) + 2^b*sum(x),
+//        v = 128 + q * 2^P,   P = 7 - b   (exact: v <= 255)
+//    Two such values share a dword and meet a dword holding the two matching
+//    raw bf16 x values, so one v_dot2c_f32_bf16 adds v_lo*x_lo + v_hi*x_hi
+//    into an fp32 accumulator.  Over a chunk that is
+//        D = 128*sum(x) + 2^P * sum(q*x),
 //    and the affine fold s*sum(q*x) + z*sum(x) (quantized.h, qdot) becomes
-//        s*D + (z - 2^b*s) * sum(x).
-//    The offset 2^b is at most ~2x the mean code, so the cancellation costs
+//        2^-P * s*D + (z - 2^b*s) * sum(x)        (2^b = 128 * 2^-P).
+//    The offset 2^b is about twice the mean code, so the cancellation costs
 //    about one bit of the fp32 accumulator.
 //
 //  * fp32 path (b = 8, and the fused silu tail whose input is not bf16): each
@@ -37,7 +37,7 @@ namespace qmvk {
 #define QMV_WAVES_PER_BLOCK 4
 #endif
 #ifndef QMV_NT_LOADS
-#define QMV_NT_LOADS 0
+#define QMV_NT_LOADS 1
 #endif
 
 constexpr int kWave = 64;
@@ -70,6 +70,31 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// Pair building is (w >> sh) & mask | magic.  With both constants as 32-bit
+// literals the compiler must split it into v_and_b32 + v_or_b32 (a VOP3
+// encoding holds no literal on gfx9); with the mask in an SGPR and the magic
+// in a VGPR it selects one v_and_or_b32.  These empty asm statements, run
+// once per kernel, hide the values so they stay in registers.
+__device__ __forceinline__ uint32_t opaque_sgpr(uint32_t v) {
+  asm volatile("" : "+s"(v));
+  return v;
+}
+__device__ __forceinline__ uint32_t opaque_vgpr(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+struct PairConsts {
+  uint32_t mask;    // SGPR
+  uint32_t magic;   // VGPR
+};
+
+template <int BITS>
+__device__ __forceinline__ PairConsts pair_consts() {
+  const uint32_t m = BITS == 4 ? 0x00780078u : BITS == 2 ? 0x00600060u : 0u;
+  return PairConsts{opaque_sgpr(m), opaque_vgpr(kMagic2)};
 }
 
 // Shift left for positive amounts, right for negative (compile-time amount).
@@ -114,19 +139,19 @@ struct PairPlan {
 };
 
 template <int BITS, int I>
-__device__ __forceinline__ uint32_t make_pair(const uint32_t (&w)[BITS]) {
+__device__ __forceinline__ uint32_t make_pair(const uint32_t (&w)[BITS], PairConsts k) {
   constexpr int P = PairPlan<BITS>::P;
   if constexpr (BITS == 4) {
     constexpr int d = I >> 2, j = I & 3;
     // code j at bit 4j -> bit 3; code j+4 at bit 4j+16 -> bit 19
-    return (shl_signed<3 - 4 * j>(w[d]) & 0x00780078u) | kMagic2;
+    return (shl_signed<3 - 4 * j>(w[d]) & k.mask) | k.magic;
   } else if constexpr (BITS == 2) {
     constexpr int d = I >> 3, j = I & 7;
     // code j at bit 2j -> bit 5; code j+8 at bit 2j+16 -> bit 21
-    return (shl_signed<5 - 2 * j>(w[d]) & 0x00600060u) | kMagic2;
+    return (shl_signed<5 - 2 * j>(w[d]) & k.mask) | k.magic;
   } else {
     constexpr int klo = PairPlan<BITS>::lo(I), khi = PairPlan<BITS>::hi(I);
-    return (code_at<BITS, klo>(w) << P) | (code_at<BITS, khi>(w) << (16 + P)) | kMagic2;
+    return (code_at<BITS, klo>(w) << P) | (code_at<BITS, khi>(w) << (16 + P)) | k.magic;
   }
 }
 
@@ -187,12 +212,34 @@ __device__ __forceinline__ void load_chunk(const uint32_t *__restrict__ p, uint3
 
 // ----------------------------------------------------------------------------
 // Wave reduction of V values per lane (V a power of two, V <= 64).  A
-// butterfly that halves the value count at each step: lanes in the upper
-// half of each xor pair keep the upper half of the values.  Every value is
-// summed over the same lane tree (pairs by lane bit 5, then 4, ...), so the
-// result for a value does not depend on its index.  On return lane l holds
-// the total of value index reduce_index<V>(l); all lanes of a group agree.
+// transposing butterfly over lane bits 5, 4, 3, ...: at each step the lanes
+// whose bit is set keep the upper half of the values, the others the lower
+// half, so the value count halves; the remaining lane bits are then summed
+// out.  Bits 5 and 4 use the gfx950 v_permlane32_swap / v_permlane16_swap
+// (which exchange whole half-waves / rows, so no select is needed), bits 3..0
+// use DPP moves fused into the adds.  Every value is summed over the same
+// lane tree, so its result does not depend on its index.  On return lane l
+// holds the total of value reduce_index<V>(l); all lanes of a group agree.
 // ----------------------------------------------------------------------------
+__device__ __forceinline__ void swap32(float &a, float &b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap16(float &a, float &b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+constexpr int kDppXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppRor8 = 0x128;     // row_ror:8 == xor 8 within a 16-lane row
+
 template <int V>
 __device__ __forceinline__ float wave_reduce_many(float (&v)[V], int lane) {
   static_assert((V & (V - 1)) == 0 && V >= 1 && V <= 64, "V must be a power of two");
@@ -204,18 +251,47 @@ __device__ __forceinline__ float wave_reduce_many(float (&v)[V], int lane) {
     constexpr int step = decltype(t)::value;
     constexpr int half = V >> (step + 1);
     constexpr int off = 32 >> step;
-    const bool upper = (lane & off) != 0;
 #pragma unroll
     for (int i = 0; i < half; ++i) {
-      float keep = upper ? cur[half + i] : cur[i];
-      float send = upper ? cur[i] : cur[half + i];
-      float recv = __shfl_xor(send, off, kWave);
-      cur[i] = keep + recv;
+      float a = cur[i], b = cur[half + i];
+      if constexpr (off == 32) {
+        swap32(a, b);
+        cur[i] = a + b;
+      } else if constexpr (off == 16) {
+        swap16(a, b);
+        cur[i] = a + b;
+      } else {
+        const bool upper = (lane & off) != 0;
+        const float keep = upper ? b : a;
+        const float send = upper ? a : b;
+        float recv;
+        if constexpr (off == 8) recv = dpp<kDppRor8>(send);
+        else recv = __shfl_xor(send, off, kWave);
+        cur[i] = keep + recv;
+      }
     }
   });
   float r = cur[0];
-#pragma unroll
-  for (int off = 32 >> LOGV; off >= 1; off >>= 1) r += __shfl_xor(r, off, kWave);
+  static_for<LOGV, 6>([&](auto t) {
+    constexpr int off = 32 >> decltype(t)::value;
+    if constexpr (off == 32) {
+      float a = r, b = r;
+      swap32(a, b);
+      r = a + b;
+    } else if constexpr (off == 16) {
+      float a = r, b = r;
+      swap16(a, b);
+      r = a + b;
+    } else if constexpr (off == 8) {
+      r += dpp<kDppRor8>(r);
+    } else if constexpr (off == 4) {
+      r += dpp<kDppHalfMirror>(r);   // all 8 lanes of the group share the value
+    } else if constexpr (off == 2) {
+      r += dpp<kDppXor2>(r);
+    } else {
+      r += dpp<kDppXor1>(r);
+    }
+  });
   return r;
 }
 

@@ -51,14 +51,16 @@ __device__ __forceinline__ float raw_x(const uint32_t (&raw)[16], int k) {
   return (k & 1) ? __uint_as_float(wv & 0xFFFF0000u) : __uint_as_float(wv << 16);
 }
 
+// Pair staging: pair i of a chunk holds x[lo(i)] in its low half and x[hi(i)]
+// in its high half, both raw bf16 (one v_perm_b32 per pair).  The chunk sum
+// is taken with dot2 against (1, 1): products by 1 are exact, so it is a
+// plain fp32 sum of the 32 values in a fixed order.
 template <int BITS>
 __device__ __forceinline__ void stage_pairs_raw(const uint32_t (&raw)[16], unsigned char *lds,
                                                 int Kc, int MVtot, int m, int c) {
-  constexpr int P = PairPlan<BITS>::P;
-  const float down = 1.0f / static_cast<float>(1 << P);
   float sum = 0.0f;
 #pragma unroll
-  for (int k = 0; k < 32; ++k) sum += raw_x(raw, k);
+  for (int k = 0; k < 16; ++k) sum = dot2_bf16(raw[k], 0x3F803F80u, sum);
   uint4 *dst = reinterpret_cast<uint4 *>(lds);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -66,10 +68,10 @@ __device__ __forceinline__ void stage_pairs_raw(const uint32_t (&raw)[16], unsig
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = 4 * q + e;
-      // x * 2^-P is exact in fp32 and again in bf16 for normal x
-      const uint32_t lo = __float_as_uint(raw_x(raw, PairPlan<BITS>::lo(i)) * down) >> 16;
-      const uint32_t hi = __float_as_uint(raw_x(raw, PairPlan<BITS>::hi(i)) * down) & 0xFFFF0000u;
-      pr[e] = lo | hi;
+      const int klo = PairPlan<BITS>::lo(i), khi = PairPlan<BITS>::hi(i);
+      // v_perm_b32(S0, S1, sel): selector bytes 0-3 pick S1's bytes, 4-7 S0's
+      const uint32_t sel = ((khi & 1) ? 0x07060000u : 0x05040000u) | ((klo & 1) ? 0x0302u : 0x0100u);
+      pr[e] = __builtin_amdgcn_perm(raw[khi >> 1], raw[klo >> 1], sel);
     }
     dst[(m * 4 + q) * Kc + c] = make_uint4(pr[0], pr[1], pr[2], pr[3]);
   }
@@ -146,30 +148,46 @@ struct WaveEngine {
   int gshift;
   int lane;
   int nsteps;
+  PairConsts pk;
+  // pair path: acc = sum s*D (D carries the codes scaled by 2^P), accz =
+  // sum (z - 2^b s)*sum(x); result = 2^-P acc + accz.  fp32 path: acc only.
   float acc[RPW][MV];
+  float accz[RPW][MV];
   ChunkStep<BITS, RPW> A, B;
+
+  __device__ __forceinline__ float result(int r, int m) const {
+    if constexpr (PAIR) return fmaf(acc[r][m], 1.0f / static_cast<float>(1 << PairPlan<BITS>::P), accz[r][m]);
+    else return acc[r][m];
+  }
 
   __device__ __forceinline__ void init(int Kc_, int gshift_, int lane_) {
     Kc = Kc_;
     gshift = gshift_;
     lane = lane_;
+    pk = pair_consts<BITS>();
     nsteps = (Kc + kWave - 1) / kWave;
 #pragma unroll
     for (int r = 0; r < RPW; ++r)
 #pragma unroll
-      for (int m = 0; m < MV; ++m) acc[r][m] = 0.0f;
+      for (int m = 0; m < MV; ++m) {
+        acc[r][m] = 0.0f;
+        accz[r][m] = 0.0f;
+      }
   }
 
+  // Loads are branch-free: lanes past the row's end re-read its last chunk
+  // (compute() ignores them).  With no divergent branches around the loads
+  // the compiler's memory-counter waits stay exact, so waiting for x (loaded
+  // first) never waits for weight words that are still in flight.
   __device__ __forceinline__ void load(int step, ChunkStep<BITS, RPW> &st) const {
-    const int c = step * kWave + lane;
-    if (c < Kc) {
-      const int gi = c >> gshift;
+    // 32-bit offsets from wave-uniform row bases: one VGPR offset per load
+    const uint32_t c = static_cast<uint32_t>(min(step * kWave + lane, Kc - 1));
+    const uint32_t gi = c >> gshift;
 #pragma unroll
-      for (int r = 0; r < RPW; ++r) {
-        load_chunk<BITS>(wrow[r] + static_cast<size_t>(c) * BITS, st.w[r]);
-        st.s[r] = srow[r][gi];
-        st.b[r] = brow[r][gi];
-      }
+    for (int r = 0; r < RPW; ++r) {
+      load_chunk<BITS>(wrow[r] + c * BITS, st.w[r]);
+      st.s[r] = srow[r][gi];
+      st.b[r] = brow[r][gi];
     }
   }
 
@@ -195,9 +213,10 @@ struct WaveEngine {
         float d = 0.0f;
         static_for<0, 16>([&](auto i) {
           constexpr int I = decltype(i)::value;
-          d = dot2_bf16(make_pair<BITS, I>(st.w[r]), xp[I], d);
+          d = dot2_bf16(make_pair<BITS, I>(st.w[r], pk), xp[I], d);
         });
-        acc[r][0] = fmaf(s, d, fmaf(zc, xs, acc[r][0]));
+        acc[r][0] = fmaf(s, d, acc[r][0]);
+        accz[r][0] = fmaf(zc, xs, accz[r][0]);
       }
     } else if constexpr (PAIR) {
       // build every row's pairs once, then stream the x vectors past them
@@ -209,7 +228,7 @@ struct WaveEngine {
       for (int r = 0; r < RPW; ++r) {
         sc[r] = bf16_to_f32(st.s[r]);
         zc[r] = fmaf(-static_cast<float>(1 << BITS), sc[r], bf16_to_f32(st.b[r]));  // z - 2^b s
-        static_for<0, 16>([&](auto i) { pr[r][decltype(i)::value] = make_pair<BITS, decltype(i)::value>(st.w[r]); });
+        static_for<0, 16>([&](auto i) { pr[r][decltype(i)::value] = make_pair<BITS, decltype(i)::value>(st.w[r], pk); });
       }
 #pragma unroll
       for (int m = 0; m < MV; ++m) {
@@ -226,7 +245,8 @@ struct WaveEngine {
             float d = 0.0f;
 #pragma unroll
             for (int i = 0; i < 16; ++i) d = dot2_bf16(pr[r][i], xp[i], d);
-            acc[r][m] = fmaf(sc[r], d, fmaf(zc[r], xs, acc[r][m]));
+            acc[r][m] = fmaf(sc[r], d, acc[r][m]);
+            accz[r][m] = fmaf(zc[r], xs, accz[r][m]);
           }
         }
       }
@@ -283,10 +303,11 @@ struct WaveEngine {
     }
   }
 
-  // Issue the first two steps' loads (before x staging).
+  // Issue the first two steps' loads (before x staging); with one step the
+  // second load re-reads cached words and is never used.
   __device__ __forceinline__ void prefetch() {
     load(0, A);
-    if (nsteps > 1) load(1, B);
+    load(1, B);
   }
 
   __device__ __forceinline__ void run(const unsigned char *lds, int MVtot, int nv) {
@@ -351,26 +372,12 @@ __global__ __launch_bounds__(kBlock) void qmv_kernel(QmvArgs a) {
   // loaded BEFORE the weight prefetch: memory counters retire in issue
   // order, so converting it then waits only for x, not for the weights.
   const int items = (XIN == XIN_SILU) ? Kc : a.M * Kc;
-  const int it0 = threadIdx.x;
   uint32_t raw0[16], raw1[16];
-  if (it0 < items) {
-    if constexpr (XIN == XIN_SILU) {
-      load_x_chunk(a.x + static_cast<size_t>(it0) * 32, raw0);
-      load_x_chunk(a.up + static_cast<size_t>(it0) * 32, raw1);
-    } else {
-      load_x_chunk(a.x + static_cast<size_t>(it0) * 32, raw0);   // m*K + c*32 == it*32
-    }
-  }
-  eng.prefetch();
-  for (int it = it0; it < items; it += kBlock) {
-    if (it != it0) {
-      if constexpr (XIN == XIN_SILU) {
-        load_x_chunk(a.x + static_cast<size_t>(it) * 32, raw0);
-        load_x_chunk(a.up + static_cast<size_t>(it) * 32, raw1);
-      } else {
-        load_x_chunk(a.x + static_cast<size_t>(it) * 32, raw0);
-      }
-    }
+  auto load_item = [&](int it) {
+    load_x_chunk(a.x + static_cast<size_t>(it) * 32, raw0);   // m*K + c*32 == it*32
+    if constexpr (XIN == XIN_SILU) load_x_chunk(a.up + static_cast<size_t>(it) * 32, raw1);
+  };
+  auto stage_item = [&](int it) {
     if constexpr (XIN == XIN_SILU) {
       stage_silu_raw(raw0, raw1, smem, Kc, it);
     } else {
@@ -378,6 +385,18 @@ __global__ __launch_bounds__(kBlock) void qmv_kernel(QmvArgs a) {
       if constexpr (PAIR) stage_pairs_raw<BITS>(raw0, smem, Kc, MV, m, c);
       else stage_f32_raw(raw0, smem, Kc, MV, m, c);
     }
+  };
+  // First item: an unconditional (clamped) load issued before the weight
+  // prefetch and pinned there, then staged by every thread (threads past the
+  // end restage the last item: identical bytes to identical addresses).
+  const int it0 = threadIdx.x;
+  load_item(min(it0, items - 1));
+  __builtin_amdgcn_sched_barrier(0);
+  eng.prefetch();
+  if (wid * kWave < items) stage_item(min(it0, items - 1));   // wave-uniform
+  for (int it = it0 + kBlock; it < items; it += kBlock) {
+    load_item(it);
+    stage_item(it);
   }
   __syncthreads();
 
@@ -390,7 +409,7 @@ __global__ __launch_bounds__(kBlock) void qmv_kernel(QmvArgs a) {
 #pragma unroll
   for (int r = 0; r < RPW; ++r)
 #pragma unroll
-    for (int m = 0; m < MV; ++m) vals[r * MV + m] = eng.acc[r][m];
+    for (int m = 0; m < MV; ++m) vals[r * MV + m] = eng.result(r, m);
   const float tot = wave_reduce_many<V>(vals, lane);
   if (reduce_leader<V>(lane)) {
     const int idx = reduce_index<V>(lane);
@@ -521,7 +540,7 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(GatherArgs a) {
 #pragma unroll
     for (int r = 0; r < RPW; ++r)
 #pragma unroll
-      for (int m = 0; m < MV; ++m) vals[r * MV + m] = eng.acc[r][m];
+      for (int m = 0; m < MV; ++m) vals[r * MV + m] = eng.result(r, m);
     const float tot = wave_reduce_many<V>(vals, lane);
     if (reduce_leader<V>(lane)) {
       const int idx = reduce_index<V>(lane);
