@@ -1,17 +1,24 @@
 #!/usr/bin/env python3
-"""Benchmark: affine group-quantized qmv, 4-bit codes, group 64,
-W [14336, 4096], batch 1, on one MI355X.
+"""Benchmark the affine group-quantized matvec kernels on one MI355X.
 
-One step = one qmv call (stage x, stream the packed weight, unpack, dot,
-fold scales/biases, reduce, store) over one set of device-resident inputs.
-Steps rotate over enough distinct weight copies (>= 512 MB in total) that the
-256 MB last-level cache cannot serve a repeat.  Time is taken with HIP events
-on the stream the kernel runs on, around the K timed launches.
+Default: the 4-bit, group-64 qmv of W [14336, 4096] at batch 1 (the headline
+workload), one JSON line on stdout.  `--workload NAME` times another
+workload, `--all` prints one line per workload, `--list` names them.
 
-Prints ONE JSON line.  Extra modes for profiling runs:
+One step = one call of the workload's entry point(s) on one set of
+device-resident inputs (for the FFN step: the gate/up launch and the fused
+down-projection launch).  Steps rotate over enough distinct copies of the
+inputs (>= 512 MB in total) that the 256 MB last-level cache cannot serve a
+repeat.  The K timed steps are captured into one HIP graph and replayed, so
+the host's per-launch cost (several microseconds through Python) does not
+starve the GPU; time is taken with HIP events on the replay stream.  The
+eager (host-launched) time per step is reported beside it.  Bytes are
+algorithmic: packed weights, bf16 scales and biases, activations and
+outputs, each counted once per step.
+
+Other modes (profiling aids):
   --no-cpu-baseline   skip the CPU oracle timing
-  --copy-calibration  time a plain device copy of known size (for counter
-                      scaling) instead of the qmv workload
+  --copy-calibration  run a plain 256 MiB device copy (counter scaling)
 """
 from __future__ import annotations
 
@@ -30,9 +37,10 @@ if ROOT not in sys.path:
 
 METRIC = "qmv GB/s & % of HBM peak, 4-bit g64 N=14336 K=4096 batch 1"
 HBM_PEAK_GBS = 8000.0
-PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "qmv_b4_g64_14336x4096_traffic.md")
+PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [os.path.join(ROOT, "bit_affine_quantized_amd", "csrc", f)
                   for f in ("qmv_device.h", "qmv_kernels.h", "qmv_api.hip")]
+ROTATE_BYTES = 512e6
 
 
 def kernel_source_hash() -> str:
@@ -43,16 +51,17 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(N, K, bits, g, M) -> int:
-    """Packed W + bf16 scales and biases + bf16 x + bf16 y, each once."""
-    return N * K * bits // 8 + 2 * 2 * N * (K // g) + 2 * M * K + 2 * M * N
+def qbytes(N, K, bits, g):
+    """Packed weight + bf16 scales + bf16 biases."""
+    return N * K * bits // 8 + 2 * 2 * N * (K // g)
 
 
-def read_traffic(src_hash: str):
-    """HBM bytes per launch from the committed counter summary, or None if
-    the summary is missing or was taken on different kernel sources."""
+def read_traffic(workload: str, src_hash: str):
+    """HBM bytes per launch from the committed counter summary for this
+    workload, or None if absent or taken on different kernel sources."""
+    path = os.path.join(PROFILE_DIR, f"traffic_{workload}.md")
     try:
-        text = open(PROFILE_TRAFFIC).read()
+        text = open(path).read()
     except OSError:
         return None
     m_hash = re.search(r"kernel_source_hash:\s*([0-9a-f]+)", text)
@@ -62,29 +71,302 @@ def read_traffic(src_hash: str):
     return float(m_val.group(1))
 
 
-def cpu_baseline(N, K, bits, g, M, budget_s=10.0):
-    """The oracle (plain C, fp64, one thread) on the same workload shape."""
+# --------------------------------------------------------------- workloads
+class Workload:
+    """name, algorithmic bytes per step, and setup(dev) -> (step(i), check)."""
+
+    def __init__(self, name, nbytes, setup, launches=1, oracle_fn=None):
+        self.name, self.nbytes, self.setup = name, nbytes, setup
+        self.launches, self.oracle_fn = launches, oracle_fn
+
+
+def _dev_bf16(torch, a, dev):
     import numpy as np
+    return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
 
-    import oracle
+
+def make_qmv(N, K, bits, g, M, name):
+    nbytes = qbytes(N, K, bits, g) + 2 * M * K + 2 * M * N
+
+    def setup(dev):
+        import torch
+        import bit_affine_quantized_amd as q
+        import synth
+        w = torch.from_numpy(synth.weight((N, K))).to(dev)
+        w_q, s, b = q.qmv_pack(w, g, bits)
+        del w
+        x = _dev_bf16(torch, synth.activation_bf16((M, K)), dev)
+        sets = max(2, math.ceil(ROTATE_BYTES / nbytes))
+        bufs = [(x.clone(), w_q.clone(), s.clone(), b.clone(),
+                 torch.empty((M, N), dtype=torch.bfloat16, device=dev))
+                for _ in range(sets)]
+
+        def step(i, stream):
+            xb, wb, sb, bb, yb = bufs[i % sets]
+            q.qmv(xb, wb, sb, bb, group_size=g, bits=bits, y=yb, stream=stream)
+        return step, sets
+
+    def cpu(budget_s):
+        import oracle
+        import synth
+        w_q, s, b = oracle.quantize_pack(synth.weight((N, K)), g, bits)
+        x = synth.activation_bf16((M, K))
+        return lambda: oracle.qmv(x, w_q, s, b, g, bits), \
+            f"full {N}x{K} b{bits} g{g} M={M} qmv"
+    return Workload(name, nbytes, setup, 1, cpu)
+
+
+def make_gate_up(N, K, bits, g, name):
+    nbytes = 2 * qbytes(N, K, bits, g) + 2 * K + 2 * 2 * N
+
+    def setup(dev):
+        import torch
+        import bit_affine_quantized_amd as q
+        import synth
+        packs = []
+        for seed in (synth.SEED_W, synth.SEED_UP):
+            w = torch.from_numpy(synth.weight((N, K), seed)).to(dev)
+            packs.append(q.qmv_pack(w, g, bits))
+            del w
+        x = _dev_bf16(torch, synth.activation_bf16((K,)), dev)
+        sets = max(2, math.ceil(ROTATE_BYTES / nbytes))
+        bufs = [(x.clone(), tuple(t.clone() for t in packs[0]),
+                 tuple(t.clone() for t in packs[1]),
+                 torch.empty(N, dtype=torch.bfloat16, device=dev),
+                 torch.empty(N, dtype=torch.bfloat16, device=dev))
+                for _ in range(sets)]
+
+        def step(i, stream):
+            xb, gw, uw, gy, uy = bufs[i % sets]
+            q.qmv_gate_up(xb, gw, uw, group_size=g, bits=bits, gate_y=gy,
+                          up_y=uy, stream=stream)
+        return step, sets
+    return Workload(name, nbytes, setup, 1)
+
+
+def make_silu_down(N, K, bits, g, name):
+    """W_down [N, K]: gate/up [K], residual and y [N]."""
+    nbytes = qbytes(N, K, bits, g) + 2 * 2 * K + 2 * 2 * N
+
+    def setup(dev):
+        import torch
+        import bit_affine_quantized_amd as q
+        import synth
+        w = torch.from_numpy(synth.weight((N, K), synth.SEED_DOWN)).to(dev)
+        pack = q.qmv_pack(w, g, bits)
+        del w
+        gate = _dev_bf16(torch, synth.activation_bf16((K,), 1), dev)
+        up = _dev_bf16(torch, synth.activation_bf16((K,), 2), dev)
+        xr = _dev_bf16(torch, synth.activation_bf16((N,), synth.SEED_XRESID),
+                       dev)
+        sets = max(2, math.ceil(ROTATE_BYTES / nbytes))
+        bufs = [(gate.clone(), up.clone(), xr.clone(),
+                 tuple(t.clone() for t in pack),
+                 torch.empty(N, dtype=torch.bfloat16, device=dev))
+                for _ in range(sets)]
+
+        def step(i, stream):
+            gb, ub, rb, wd, yb = bufs[i % sets]
+            q.qmv_silu_gate_resid(gb, ub, rb, *wd, group_size=g, bits=bits,
+                                  y=yb, stream=stream)
+        return step, sets
+    return Workload(name, nbytes, setup, 1)
+
+
+def make_ffn(N, K, bits, g, name):
+    """gate/up [N, K] in one launch, then down [K, N] with silu and residual."""
+    nbytes = (2 * qbytes(N, K, bits, g) + 2 * K + 2 * 2 * N) + \
+        (qbytes(K, N, bits, g) + 2 * 2 * N + 2 * 2 * K)
+
+    def setup(dev):
+        import torch
+        import bit_affine_quantized_amd as q
+        import synth
+        packs = []
+        for seed, shape in ((synth.SEED_W, (N, K)), (synth.SEED_UP, (N, K)),
+                            (synth.SEED_DOWN, (K, N))):
+            w = torch.from_numpy(synth.weight(shape, seed)).to(dev)
+            packs.append(q.qmv_pack(w, g, bits))
+            del w
+        x = _dev_bf16(torch, synth.activation_bf16((K,)), dev)
+        xr = _dev_bf16(torch, synth.activation_bf16((K,), synth.SEED_XRESID),
+                       dev)
+        sets = max(2, math.ceil(ROTATE_BYTES / nbytes))
+        bufs = [(x.clone(), xr.clone(),
+                 [tuple(t.clone() for t in p) for p in packs],
+                 torch.empty(N, dtype=torch.bfloat16, device=dev),
+                 torch.empty(N, dtype=torch.bfloat16, device=dev),
+                 torch.empty(K, dtype=torch.bfloat16, device=dev))
+                for _ in range(sets)]
+
+        def step(i, stream):
+            xb, rb, (gw, uw, dw), gy, uy, yb = bufs[i % sets]
+            q.qmv_gate_up(xb, gw, uw, group_size=g, bits=bits, gate_y=gy,
+                          up_y=uy, stream=stream)
+            q.qmv_silu_gate_resid(gy, uy, rb, *dw, group_size=g, bits=bits,
+                                  y=yb, stream=stream)
+        return step, sets
+    return Workload(name, nbytes, setup, 2)
+
+
+def make_moe(E, N, K, bits, g, T, top, sorted_idx, name):
+    import numpy as np
     import synth
+    lhs, rhs = synth.moe_indices(T, top, E)
+    used = len(np.unique(rhs))
+    P = T * top
+    # distinct experts' weights once, x, y, indices
+    nbytes = used * qbytes(N, K, bits, g) + 2 * T * K + 2 * P * N + 2 * 4 * P
 
-    w = synth.weight((N, K))
-    w_q, s, b = oracle.quantize_pack(w, g, bits)
-    x = synth.activation_bf16((M, K))
+    def setup(dev):
+        import torch
+        import bit_affine_quantized_amd as q
+        ws, ss, bs = [], [], []
+        for e in range(E):
+            w = torch.from_numpy(synth.weight((N, K), 1000 + e)).to(dev)
+            a, b_, c = q.qmv_pack(w, g, bits)
+            ws.append(a), ss.append(b_), bs.append(c)
+            del w
+        w_q, s, b = torch.stack(ws), torch.stack(ss), torch.stack(bs)
+        del ws, ss, bs
+        x = _dev_bf16(torch, synth.activation_bf16((T, 1, K)), dev)
+        l_np, r_np = lhs.ravel(), rhs.ravel()
+        if sorted_idx:
+            perm = np.argsort(r_np, kind="stable")
+            l_np, r_np = l_np[perm], r_np[perm]
+        li = torch.from_numpy(l_np.astype(np.int32)).to(dev)
+        ri = torch.from_numpy(r_np.astype(np.int32)).to(dev)
+        full = E * qbytes(N, K, bits, g)
+        sets = max(2, math.ceil(ROTATE_BYTES / full))
+        bufs = [(x.clone(), w_q.clone(), s.clone(), b.clone(), li.clone(),
+                 ri.clone(), torch.empty((P, 1, N), dtype=torch.bfloat16,
+                                         device=dev)) for _ in range(sets)]
+
+        def step(i, stream):
+            xb, wb, sb, bb, lb, rb, yb = bufs[i % sets]
+            q.gather_qmv(xb, wb, sb, bb, lb, rb, group_size=g, bits=bits,
+                         sorted_indices=sorted_idx, y=yb, stream=stream)
+        return step, sets
+    return Workload(name, nbytes, setup, 1)
+
+
+def workloads():
+    import synth
+    W = {}
+    h = synth.HEADLINE
+    W[h["name"]] = make_qmv(h["N"], h["K"], h["bits"], h["group"], 1, h["name"])
+    t = synth.TINY
+    W[t["name"]] = make_qmv(t["N"], t["K"], t["bits"], t["group"], 1, t["name"])
+    for M in (1, 4):
+        n = f"decode_qmv_4096x4096_b4_g64_m{M}"
+        W[n] = make_qmv(4096, 4096, 4, 64, M, n)
+    for bits in (2, 3, 5, 6, 8):
+        for g in (32, 64, 128):
+            n = f"qmv_14336x4096_b{bits}_g{g}_m1"
+            W[n] = make_qmv(14336, 4096, bits, g, 1, n)
+    W["ffn_gate_up_14336x4096_b8_g64"] = make_gate_up(
+        14336, 4096, 8, 64, "ffn_gate_up_14336x4096_b8_g64")
+    W["ffn_down_silu_resid_4096x14336_b8_g64"] = make_silu_down(
+        4096, 14336, 8, 64, "ffn_down_silu_resid_4096x14336_b8_g64")
+    W["ffn_step_14336x4096_b8_g64"] = make_ffn(
+        14336, 4096, 8, 64, "ffn_step_14336x4096_b8_g64")
+    m = synth.MOE
+    for srt in (False, True):
+        n = f"moe_gather_64x2048x2048_b4_g64_t16_top8_{'sorted' if srt else 'unsorted'}"
+        W[n] = make_moe(m["E"], m["N"], m["K"], m["bits"], m["group"],
+                        m["tokens"], m["top_k"], srt, n)
+    return W
+
+
+def cpu_baseline(wl: Workload, budget_s=10.0):
+    fn, what = wl.oracle_fn(budget_s)
     reps, t0 = 0, time.perf_counter()
     while True:
-        oracle.qmv(x, w_q, s, b, g, bits)
+        fn()
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
             break
     per = el / reps
-    return {"value": algorithmic_bytes(N, K, bits, g, M) / per / 1e9,
-            "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"full {N}x{K} b{bits} g{g} M={M} qmv, {reps} runs "
-                      f"({el:.1f} s), fp64 dequant-and-dot, 1 thread",
-            "ms_per_call": per * 1e3}
+    return {"value": round(wl.nbytes / per / 1e9, 4), "unit": "GB/s",
+            "cores": 1, "kind": "oracle",
+            "sample": f"{what}, {reps} runs in {el:.1f} s (plain C, fp64 "
+                      "dequant-and-dot, 1 thread)"}
+
+
+def _time_eager(step, steps, stream):
+    import torch
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(steps):
+        step(i, stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
+def _time_graph(step, steps, warmup):
+    """Capture `steps` steps into one HIP graph and time a replay: the GPU
+    runs the launches back to back with no host launch cost in between."""
+    import torch
+    side = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        cs = torch.cuda.current_stream()
+        for i in range(steps):
+            step(i, cs)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    graph.replay()                       # warm replay
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    graph.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    del graph
+    return ms
+
+
+def run_workload(wl: Workload, steps: int, warmup: int, want_cpu: bool,
+                 use_graph: bool = True):
+    import torch
+    dev = torch.device("cuda:0")
+    step, sets = wl.setup(dev)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        step(i, stream)
+    torch.cuda.synchronize()
+    ms_eager = _time_eager(step, steps, stream)
+    ms = _time_graph(step, steps, warmup) if use_graph else ms_eager
+    gbs = wl.nbytes / (ms * 1e-3) / 1e9
+    res = {
+        "metric": METRIC if wl.name.startswith("qmv_14336x4096_b4_g64_m1")
+        else f"{wl.name} GB/s & % of HBM peak",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": round(ms, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "bytes_per_step": wl.nbytes,
+                   "launches_per_step": wl.launches,
+                   "input_sets_rotated": sets,
+                   "timing": "hip_graph_replay" if use_graph else "eager",
+                   "eager_ms_per_step": round(ms_eager, 6),
+                   "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)},
+    }
+    res["roofline"] = {"bound": "hbm", "achieved": round(gbs, 2),
+                       "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "frac": round(gbs / HBM_PEAK_GBS, 4),
+                       "traffic": read_traffic(wl.name, kernel_source_hash())}
+    res["cpu_baseline"] = cpu_baseline(wl) if (want_cpu and wl.oracle_fn) \
+        else None
+    del step
+    torch.cuda.empty_cache()
+    return res
 
 
 def copy_calibration(steps: int):
@@ -106,8 +388,13 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--all", action="store_true")
+    ap.add_argument("--list", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="time eager launches instead of a graph replay")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -116,77 +403,23 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
-    import torch
-
-    import bit_affine_quantized_amd as q
-    import synth
-
+    W = workloads()
+    if args.list:
+        for n, w in W.items():
+            print(n, w.nbytes)
+        return
     if args.copy_calibration:
         copy_calibration(args.steps)
         return
-
-    cfg = synth.HEADLINE
-    N, K, bits, g, M = cfg["N"], cfg["K"], cfg["bits"], cfg["group"], cfg["M"]
-    dev = torch.device("cuda:0")
-    nbytes = algorithmic_bytes(N, K, bits, g, M)
-    sets = max(2, math.ceil(512e6 / nbytes))
-
-    # device-resident inputs: quantize once on the device, replicate
-    w = torch.from_numpy(synth.weight((N, K))).to(dev)
-    w_q, s, b = q.qmv_pack(w, g, bits)
-    del w
-    x_bits = synth.activation_bf16((M, K))
-    x = torch.from_numpy(x_bits.view(np.int16)).to(dev).view(torch.bfloat16)
-    bufs = []
-    for _ in range(sets):
-        bufs.append((x.clone(), w_q.clone(), s.clone(), b.clone(),
-                     torch.empty((M, N), dtype=torch.bfloat16, device=dev)))
-    torch.cuda.synchronize()
-
-    stream = torch.cuda.current_stream()
-
-    def step(i):
-        xb, wb, sb, bb, yb = bufs[i % sets]
-        q.qmv(xb, wb, sb, bb, group_size=g, bits=bits, y=yb, stream=stream)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / args.steps
-    gbs = nbytes / (ms * 1e-3) / 1e9
-
-    result = {
-        "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms, 6), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": cfg["name"], "N": N, "K": K, "bits": bits,
-                   "group_size": g, "batch": M, "transpose": True,
-                   "bytes_per_step": nbytes, "weight_sets_rotated": sets,
-                   "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)},
-    }
-    traffic = read_traffic(kernel_source_hash())
-    result["roofline"] = {"bound": "hbm", "achieved": round(gbs, 2),
-                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                          "frac": round(gbs / HBM_PEAK_GBS, 4),
-                          "traffic": traffic}
-    if not args.no_cpu_baseline:
-        cb = cpu_baseline(N, K, bits, g, M)
-        cb.pop("ms_per_call", None)
-        cb["value"] = round(cb["value"], 4)
-        result["cpu_baseline"] = cb
-    else:
-        result["cpu_baseline"] = None
-    print(json.dumps(result), flush=True)
+    import synth
+    names = list(W) if args.all else [args.workload or synth.HEADLINE["name"]]
+    for n in names:
+        if n not in W:
+            print(f"unknown workload {n}; --list shows them", file=sys.stderr)
+            sys.exit(2)
+        want_cpu = not args.no_cpu_baseline and (n == synth.HEADLINE["name"])
+        print(json.dumps(run_workload(W[n], args.steps, args.warmup,
+                                      want_cpu, not args.eager)), flush=True)
 
 
 if __name__ == "__main__":

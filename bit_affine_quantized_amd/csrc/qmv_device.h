@@ -191,6 +191,13 @@ __device__ __forceinline__ T stream_load(const T *p) {
 #endif
 }
 
+// base + a 32-bit byte offset: lets the compiler use the global_load
+// "saddr + 32-bit voffset" form when the base is wave-uniform.
+template <typename T>
+__device__ __forceinline__ const T *byte_offset(const T *base, uint32_t bytes) {
+  return reinterpret_cast<const T *>(reinterpret_cast<const char *>(base) + bytes);
+}
+
 template <int BITS>
 __device__ __forceinline__ void load_chunk(const uint32_t *__restrict__ p, uint32_t (&w)[BITS]) {
   if constexpr (BITS == 4) {

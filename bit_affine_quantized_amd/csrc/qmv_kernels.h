@@ -185,9 +185,9 @@ struct WaveEngine {
     const uint32_t gi = c >> gshift;
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
-      load_chunk<BITS>(wrow[r] + c * BITS, st.w[r]);
-      st.s[r] = srow[r][gi];
-      st.b[r] = brow[r][gi];
+      load_chunk<BITS>(byte_offset(wrow[r], c * (BITS * 4)), st.w[r]);
+      st.s[r] = *byte_offset(srow[r], gi * 2);
+      st.b[r] = *byte_offset(brow[r], gi * 2);
     }
   }
 
@@ -374,8 +374,9 @@ __global__ __launch_bounds__(kBlock) void qmv_kernel(QmvArgs a) {
   const int items = (XIN == XIN_SILU) ? Kc : a.M * Kc;
   uint32_t raw0[16], raw1[16];
   auto load_item = [&](int it) {
-    load_x_chunk(a.x + static_cast<size_t>(it) * 32, raw0);   // m*K + c*32 == it*32
-    if constexpr (XIN == XIN_SILU) load_x_chunk(a.up + static_cast<size_t>(it) * 32, raw1);
+    const uint32_t off = static_cast<uint32_t>(it) * 64;   // bytes of m*K + c*32 == it*32
+    load_x_chunk(byte_offset(a.x, off), raw0);
+    if constexpr (XIN == XIN_SILU) load_x_chunk(byte_offset(a.up, off), raw1);
   };
   auto stage_item = [&](int it) {
     if constexpr (XIN == XIN_SILU) {
