@@ -85,7 +85,7 @@ template <int BITS, int MV, int XIN>
 int launch_qmv_t(const qmvk::QmvArgs &a, hipStream_t st) {
   constexpr bool PAIR = (BITS <= 6) && (XIN == qmvk::XIN_PLAIN);
   const int64_t Kc = a.K / 32;
-  const int64_t lds = (XIN == qmvk::XIN_SILU ? 1 : MV) * Kc * qmvk::stage_bytes_per_chunk<PAIR>();
+  const int64_t lds = Kc * qmvk::chunk_stride<PAIR, (XIN == qmvk::XIN_SILU ? 1 : MV)>();
   const int64_t rows = static_cast<int64_t>(a.nmat) * a.N;
   const int64_t rows_per_block = qmvk::kWavesPerBlock * kRpw;
   const int64_t blocks = (rows + rows_per_block - 1) / rows_per_block;
@@ -112,25 +112,49 @@ int launch_qmv_bits(int bits, const qmvk::QmvArgs &a, hipStream_t st) {
 
 int64_t qmv_lds_bytes(int bits, int mv, int64_t K) {
   const bool pair = bits <= 6;
-  return mv * (K / 32) * (pair ? 68 : 132);
+  return (K / 32) * (mv * (pair ? 64 : 128) + 16);
 }
 
 // ------------------------------------------------------------------ gather
-constexpr int kGatherRpw = 4;
-constexpr int kGatherMv = 8;
+#ifndef QMV_GATHER_WAVES
+#define QMV_GATHER_WAVES 8
+#endif
+#ifndef QMV_GATHER_DEPTH
+#define QMV_GATHER_DEPTH 4
+#endif
+#ifndef QMV_GATHER_RPW
+#define QMV_GATHER_RPW 2
+#endif
+constexpr int kGatherRpw = QMV_GATHER_RPW;
+constexpr int kGatherWaves = QMV_GATHER_WAVES;
+constexpr int kGatherDepth = QMV_GATHER_DEPTH;   // chunk steps in flight per wave
+// x vectors per pass over an expert's rows (fp32 staging is twice as wide)
+template <int BITS>
+constexpr int gather_mv() { return BITS <= 6 ? 4 : 2; }
 
 template <int BITS>
 int launch_gather_t(const qmvk::GatherArgs &a0, int64_t E, hipStream_t st) {
+  constexpr int kGatherMv = gather_mv<BITS>();
   qmvk::GatherArgs a = a0;
   const int64_t Kc = a.K / 32;
-  const int64_t lds = kGatherMv * Kc * qmvk::stage_bytes_per_chunk<(BITS <= 6)>();
-  const int64_t rows_per_block = qmvk::kWavesPerBlock * kGatherRpw;
-  const int64_t tiles = (a.N + rows_per_block - 1) / rows_per_block;
+  const int64_t lds = Kc * qmvk::chunk_stride<(BITS <= 6), kGatherMv>();
+  // Tiles of `tile_rows` rows: large enough that routing and x staging are
+  // paid once per many rows, small enough for ~2 workgroups per CU over the
+  // expert stack.
+  const int64_t unit = kGatherWaves * kGatherRpw;
+  int64_t tile_rows = (a.N * E + 511) / 512;
+  tile_rows = ((tile_rows + unit - 1) / unit) * unit;
+  const int64_t n_round = ((a.N + unit - 1) / unit) * unit;
+  if (tile_rows > n_round) tile_rows = n_round;
+  if (tile_rows > 4096) tile_rows = 4096;
+  if (tile_rows < unit) tile_rows = unit;
+  const int64_t tiles = (a.N + tile_rows - 1) / tile_rows;
   if (E * tiles > 0x7FFFFFFF) return fail(QMV_EUNSUPPORTED, "gather_qmv: grid too large");
   a.tiles = static_cast<int>(tiles);
-  auto kern = qmvk::gather_kernel<BITS, kGatherRpw, kGatherMv>;
+  a.tile_rows = static_cast<int>(tile_rows);
+  auto kern = qmvk::gather_kernel<BITS, kGatherRpw, kGatherMv, kGatherWaves, kGatherDepth>;
   allow_lds(kern, lds);
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(E * tiles)), dim3(qmvk::kBlock),
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(E * tiles)), dim3(kGatherWaves * qmvk::kWave),
                      static_cast<size_t>(lds), st, a);
   return check_launch("gather_qmv");
 }
@@ -261,7 +285,7 @@ int qmv_silu_gate_resid(const uint16_t *gate, const uint16_t *up, const uint16_t
   if (int rc = check_aligned("qmv_silu_gate_resid", gate, "gate")) return rc;
   if (int rc = check_aligned("qmv_silu_gate_resid", up, "up")) return rc;
   if (int rc = check_aligned("qmv_silu_gate_resid", w_q, "w_q")) return rc;
-  if ((K / 32) * 132 > kMaxLds)
+  if (qmv_lds_bytes(8, 1, K) > kMaxLds)
     return fail(QMV_EUNSUPPORTED, "qmv_silu_gate_resid: K=%lld too large", (long long)K);
   qmvk::QmvArgs a{};
   a.x = gate;
@@ -304,11 +328,7 @@ int gather_qmv(const uint16_t *x, int64_t Bx, const uint32_t *w_q, const uint16_
   if (P <= 0) return fail(QMV_EINVAL, "gather_qmv: P=%lld must be positive", (long long)P);
   if (int rc = check_aligned("gather_qmv", x, "x")) return rc;
   if (int rc = check_aligned("gather_qmv", w_q, "w_q")) return rc;
-  if (!sorted_indices && P > qmvk::kGatherListMax)
-    return fail(QMV_EUNSUPPORTED,
-                "gather_qmv: unsorted indices with P=%lld > %d pairs; pass rhs sorted (sorted_indices=1)",
-                (long long)P, qmvk::kGatherListMax);
-  if (qmv_lds_bytes(bits, kGatherMv, K) > kMaxLds)
+  if (qmv_lds_bytes(bits, bits <= 6 ? gather_mv<4>() : gather_mv<8>(), K) > kMaxLds)
     return fail(QMV_EUNSUPPORTED, "gather_qmv: K=%lld too large", (long long)K);
   if (M > (int64_t(1) << 20) || P > (int64_t(1) << 30))
     return fail(QMV_EUNSUPPORTED, "gather_qmv: M or P too large");
@@ -324,7 +344,7 @@ int gather_qmv(const uint16_t *x, int64_t Bx, const uint32_t *w_q, const uint16_
   a.K = static_cast<int>(K);
   a.M = static_cast<int>(M);
   a.gshift = gshift_of(group_size);
-  a.sorted = sorted_indices ? 1 : 0;
+  (void)sorted_indices;   // a hint only: the in-kernel routing is order-independent
   a.out_f32 = out_dtype == QMV_OUT_F32;
   a.y = y;
   hipStream_t st = static_cast<hipStream_t>(stream);

@@ -26,15 +26,24 @@ struct MatDesc {
   void *y;
 };
 
-// Bytes of LDS that a staged x vector takes per 32-code chunk.
+// Staged-x layout in LDS, chunk-major: chunk c of the staged vectors starts
+// at c * chunk_stride<PAIR, MV>(); vector m's data sits at m * vec_bytes and
+// the MV fp32 chunk sums follow, in a 16-byte tail.  Every offset inside a
+// chunk is a compile-time immediate, and the strides (80/144/272 bytes for
+// bf16 pairs, 144/272/528 for fp32) put 16 consecutive lanes on 16 distinct
+// 4-bank quads of LDS, so 128-bit reads do not conflict.
 template <bool PAIR>
-constexpr int stage_bytes_per_chunk() { return PAIR ? 64 + 4 : 128 + 4; }
+constexpr int vec_bytes() { return PAIR ? 64 : 128; }
+template <bool PAIR, int MV>
+constexpr int chunk_stride() {
+  static_assert(MV >= 1 && MV <= 4, "at most 4 staged x vectors");
+  return MV * vec_bytes<PAIR>() + 16;
+}
+template <bool PAIR>
+constexpr int stage_bytes_per_chunk() { return vec_bytes<PAIR>() + 16; }   // one vector (host sizing)
 
 // ----------------------------------------------------------------------------
-// x staging.  Pair layout: quad q (pairs 4q..4q+3) of vector m, chunk c at
-// uint4 index (m*4 + q)*Kc + c.  fp32 layout: quad q (codes 4q..4q+3) at
-// float4 index (m*8 + q)*Kc + c.  Sums at float index m*Kc + c after the
-// quads.  Consecutive lanes read consecutive 16-byte slots: no bank conflict.
+// x staging (layout above).
 // ----------------------------------------------------------------------------
 // Raw x of one chunk: 32 bf16 = 16 words.
 __device__ __forceinline__ void load_x_chunk(const uint16_t *__restrict__ xk, uint32_t (&raw)[16]) {
@@ -55,13 +64,13 @@ __device__ __forceinline__ float raw_x(const uint32_t (&raw)[16], int k) {
 // in its high half, both raw bf16 (one v_perm_b32 per pair).  The chunk sum
 // is taken with dot2 against (1, 1): products by 1 are exact, so it is a
 // plain fp32 sum of the 32 values in a fixed order.
-template <int BITS>
+template <int BITS, int MV>
 __device__ __forceinline__ void stage_pairs_raw(const uint32_t (&raw)[16], unsigned char *lds,
-                                                int Kc, int MVtot, int m, int c) {
+                                                int m, int c) {
   float sum = 0.0f;
 #pragma unroll
   for (int k = 0; k < 16; ++k) sum = dot2_bf16(raw[k], 0x3F803F80u, sum);
-  uint4 *dst = reinterpret_cast<uint4 *>(lds);
+  unsigned char *chunk = lds + c * chunk_stride<true, MV>();
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     uint32_t pr[4];
@@ -73,52 +82,51 @@ __device__ __forceinline__ void stage_pairs_raw(const uint32_t (&raw)[16], unsig
       const uint32_t sel = ((khi & 1) ? 0x07060000u : 0x05040000u) | ((klo & 1) ? 0x0302u : 0x0100u);
       pr[e] = __builtin_amdgcn_perm(raw[khi >> 1], raw[klo >> 1], sel);
     }
-    dst[(m * 4 + q) * Kc + c] = make_uint4(pr[0], pr[1], pr[2], pr[3]);
+    *reinterpret_cast<uint4 *>(chunk + m * 64 + q * 16) = make_uint4(pr[0], pr[1], pr[2], pr[3]);
   }
-  float *sums = reinterpret_cast<float *>(lds + static_cast<size_t>(MVtot) * Kc * 64);
-  sums[m * Kc + c] = sum;
+  reinterpret_cast<float *>(chunk + MV * 64)[m] = sum;
 }
 
-template <int BITS>
+template <int BITS, int MV>
 __device__ __forceinline__ void stage_pairs_chunk(const uint16_t *__restrict__ xk,
-                                                  unsigned char *lds, int Kc, int MVtot,
-                                                  int m, int c) {
+                                                  unsigned char *lds, int m, int c) {
   uint32_t raw[16];
   load_x_chunk(xk, raw);
-  stage_pairs_raw<BITS>(raw, lds, Kc, MVtot, m, c);
+  stage_pairs_raw<BITS, MV>(raw, lds, m, c);
 }
 
-__device__ __forceinline__ void store_f32_chunk(const float (&v)[32], unsigned char *lds, int Kc,
-                                                int MVtot, int m, int c) {
+template <int MV>
+__device__ __forceinline__ void store_f32_chunk(const float (&v)[32], unsigned char *lds, int m, int c) {
   float sum = 0.0f;
 #pragma unroll
   for (int k = 0; k < 32; ++k) sum += v[k];
-  float4 *dst = reinterpret_cast<float4 *>(lds);
+  unsigned char *chunk = lds + c * chunk_stride<false, MV>();
 #pragma unroll
   for (int q = 0; q < 8; ++q)
-    dst[(m * 8 + q) * Kc + c] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
-  float *sums = reinterpret_cast<float *>(lds + static_cast<size_t>(MVtot) * Kc * 128);
-  sums[m * Kc + c] = sum;
+    *reinterpret_cast<float4 *>(chunk + m * 128 + q * 16) =
+        make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+  reinterpret_cast<float *>(chunk + MV * 128)[m] = sum;
 }
 
-__device__ __forceinline__ void stage_f32_raw(const uint32_t (&raw)[16], unsigned char *lds,
-                                              int Kc, int MVtot, int m, int c) {
+template <int MV>
+__device__ __forceinline__ void stage_f32_raw(const uint32_t (&raw)[16], unsigned char *lds, int m, int c) {
   float v[32];
 #pragma unroll
   for (int k = 0; k < 32; ++k) v[k] = raw_x(raw, k);
-  store_f32_chunk(v, lds, Kc, MVtot, m, c);
+  store_f32_chunk<MV>(v, lds, m, c);
 }
 
+template <int MV>
 __device__ __forceinline__ void stage_f32_chunk(const uint16_t *__restrict__ xk, unsigned char *lds,
-                                                int Kc, int MVtot, int m, int c) {
+                                                int m, int c) {
   uint32_t raw[16];
   load_x_chunk(xk, raw);
-  stage_f32_raw(raw, lds, Kc, MVtot, m, c);
+  stage_f32_raw<MV>(raw, lds, m, c);
 }
 
 // h = silu(gate) * up in fp32 (metrale QuantWeights::gemv_silu_gate_resid).
 __device__ __forceinline__ void stage_silu_raw(const uint32_t (&graw)[16], const uint32_t (&uraw)[16],
-                                               unsigned char *lds, int Kc, int c) {
+                                               unsigned char *lds, int c) {
   float v[32];
 #pragma unroll
   for (int k = 0; k < 32; ++k) {
@@ -126,18 +134,139 @@ __device__ __forceinline__ void stage_silu_raw(const uint32_t (&graw)[16], const
     const float u = raw_x(uraw, k);
     v[k] = g / (1.0f + __expf(-g)) * u;
   }
-  store_f32_chunk(v, lds, Kc, 1, 0, c);
+  store_f32_chunk<1>(v, lds, 0, c);
 }
 
 // ----------------------------------------------------------------------------
 // The streaming dot-product engine for one wave: RPW rows x MV x-vectors.
 // ----------------------------------------------------------------------------
+// One chunk step of RPW rows: the chunk words and each row's scale and bias
+// bf16 bits.  (Separate registers: packing the two into one register with
+// d16/d16_hi loads chains the second load on the first and measured slower.)
 template <int BITS, int RPW>
 struct ChunkStep {
   uint32_t w[RPW][BITS];
   uint16_t s[RPW];
   uint16_t b[RPW];
+  __device__ __forceinline__ float scale(int r) const { return bf16_to_f32(s[r]); }
+  __device__ __forceinline__ float bias(int r) const { return bf16_to_f32(b[r]); }
 };
+
+// ----------------------------------------------------------------------------
+// One 32-code chunk of RPW rows against MV staged x vectors (chunk c of the
+// row; the caller has checked c < Kc).
+// ----------------------------------------------------------------------------
+template <int BITS, int RPW, int MV, bool PAIR>
+__device__ __forceinline__ void accumulate_chunk(const ChunkStep<BITS, RPW> &st, const unsigned char *lds,
+                                                 int nv, int c, PairConsts pk,
+                                                 float (&acc)[RPW][MV], float (&accz)[RPW][MV]) {
+  const unsigned char *chunk = lds + c * chunk_stride<PAIR, MV>();
+  const float *sums = reinterpret_cast<const float *>(chunk + MV * vec_bytes<PAIR>());
+  if constexpr (PAIR && MV == 1) {
+    // one x vector: keep its pairs in registers, build one row's pairs at a time
+    uint32_t xp[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 v = *reinterpret_cast<const uint4 *>(chunk + q * 16);
+      xp[4 * q] = v.x; xp[4 * q + 1] = v.y; xp[4 * q + 2] = v.z; xp[4 * q + 3] = v.w;
+    }
+    const float xs = sums[0];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const float s = st.scale(r);
+      const float zc = fmaf(-static_cast<float>(1 << BITS), s, st.bias(r));  // z - 2^b s
+      float d = 0.0f;
+      static_for<0, 16>([&](auto i) {
+        constexpr int I = decltype(i)::value;
+        d = dot2_bf16(make_pair<BITS, I>(st.w[r], pk), xp[I], d);
+      });
+      acc[r][0] = fmaf(s, d, acc[r][0]);
+      accz[r][0] = fmaf(zc, xs, accz[r][0]);
+    }
+  } else if constexpr (PAIR) {
+    // build every row's pairs once, then stream the x vectors past them
+    uint32_t pr[RPW][16];
+    float sc[RPW], zc[RPW];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      sc[r] = st.scale(r);
+      zc[r] = fmaf(-static_cast<float>(1 << BITS), sc[r], st.bias(r));  // z - 2^b s
+      static_for<0, 16>([&](auto i) { pr[r][decltype(i)::value] = make_pair<BITS, decltype(i)::value>(st.w[r], pk); });
+    }
+#pragma unroll
+    for (int m = 0; m < MV; ++m) {
+      if (m < nv) {
+        uint32_t xp[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint4 v = *reinterpret_cast<const uint4 *>(chunk + m * 64 + q * 16);
+          xp[4 * q] = v.x; xp[4 * q + 1] = v.y; xp[4 * q + 2] = v.z; xp[4 * q + 3] = v.w;
+        }
+        const float xs = sums[m];
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+          float d = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) d = dot2_bf16(pr[r][i], xp[i], d);
+          acc[r][m] = fmaf(sc[r], d, acc[r][m]);
+          accz[r][m] = fmaf(zc[r], xs, accz[r][m]);
+        }
+      }
+      // keep one vector's x pairs live at a time (no hoisting of the next
+      // vector's LDS reads above these products)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    if constexpr (MV == 1) {
+      // one x vector: keep it in registers, convert one row's codes at a time
+      float xf[32];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float4 v = *reinterpret_cast<const float4 *>(chunk + q * 16);
+        xf[4 * q] = v.x; xf[4 * q + 1] = v.y; xf[4 * q + 2] = v.z; xf[4 * q + 3] = v.w;
+      }
+      const float xs = sums[0];
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        float d0 = 0.0f, d1 = 0.0f;
+        static_for<0, 16>([&](auto h) {
+          constexpr int k = 2 * decltype(h)::value;
+          d0 = fmaf(code_f32<BITS, k>(st.w[r]), xf[k], d0);
+          d1 = fmaf(code_f32<BITS, k + 1>(st.w[r]), xf[k + 1], d1);
+        });
+        acc[r][0] = fmaf(st.scale(r), d0 + d1, fmaf(st.bias(r), xs, acc[r][0]));
+      }
+    } else {
+      float qf[RPW][32];
+#pragma unroll
+      for (int r = 0; r < RPW; ++r)
+        static_for<0, 32>([&](auto k) { qf[r][decltype(k)::value] = code_f32<BITS, decltype(k)::value>(st.w[r]); });
+#pragma unroll
+      for (int m = 0; m < MV; ++m) {
+        if (m < nv) {
+          float xf[32];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const float4 v = *reinterpret_cast<const float4 *>(chunk + m * 128 + q * 16);
+            xf[4 * q] = v.x; xf[4 * q + 1] = v.y; xf[4 * q + 2] = v.z; xf[4 * q + 3] = v.w;
+          }
+          const float xs = sums[m];
+#pragma unroll
+          for (int r = 0; r < RPW; ++r) {
+            float d0 = 0.0f, d1 = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 32; k += 2) {
+              d0 = fmaf(qf[r][k], xf[k], d0);
+              d1 = fmaf(qf[r][k + 1], xf[k + 1], d1);
+            }
+            acc[r][m] = fmaf(st.scale(r), d0 + d1, fmaf(st.bias(r), xs, acc[r][m]));
+          }
+        }
+      }
+    }
+  }
+}
+
 
 template <int BITS, int RPW, int MV, bool PAIR>
 struct WaveEngine {
@@ -192,115 +321,10 @@ struct WaveEngine {
   }
 
   __device__ __forceinline__ void compute(int step, const ChunkStep<BITS, RPW> &st,
-                                          const unsigned char *lds, int MVtot, int nv) {
+                                          const unsigned char *lds, int nv) {
     const int c = step * kWave + lane;
     if (c >= Kc) return;
-    if constexpr (PAIR && MV == 1) {
-      // one x vector: keep its pairs in registers, build one row's pairs at a time
-      const uint4 *xq = reinterpret_cast<const uint4 *>(lds);
-      const float *sums = reinterpret_cast<const float *>(lds + static_cast<size_t>(MVtot) * Kc * 64);
-      uint32_t xp[16];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint4 v = xq[q * Kc + c];
-        xp[4 * q] = v.x; xp[4 * q + 1] = v.y; xp[4 * q + 2] = v.z; xp[4 * q + 3] = v.w;
-      }
-      const float xs = sums[c];
-#pragma unroll
-      for (int r = 0; r < RPW; ++r) {
-        const float s = bf16_to_f32(st.s[r]);
-        const float zc = fmaf(-static_cast<float>(1 << BITS), s, bf16_to_f32(st.b[r]));  // z - 2^b s
-        float d = 0.0f;
-        static_for<0, 16>([&](auto i) {
-          constexpr int I = decltype(i)::value;
-          d = dot2_bf16(make_pair<BITS, I>(st.w[r], pk), xp[I], d);
-        });
-        acc[r][0] = fmaf(s, d, acc[r][0]);
-        accz[r][0] = fmaf(zc, xs, accz[r][0]);
-      }
-    } else if constexpr (PAIR) {
-      // build every row's pairs once, then stream the x vectors past them
-      const uint4 *xq = reinterpret_cast<const uint4 *>(lds);
-      const float *sums = reinterpret_cast<const float *>(lds + static_cast<size_t>(MVtot) * Kc * 64);
-      uint32_t pr[RPW][16];
-      float sc[RPW], zc[RPW];
-#pragma unroll
-      for (int r = 0; r < RPW; ++r) {
-        sc[r] = bf16_to_f32(st.s[r]);
-        zc[r] = fmaf(-static_cast<float>(1 << BITS), sc[r], bf16_to_f32(st.b[r]));  // z - 2^b s
-        static_for<0, 16>([&](auto i) { pr[r][decltype(i)::value] = make_pair<BITS, decltype(i)::value>(st.w[r], pk); });
-      }
-#pragma unroll
-      for (int m = 0; m < MV; ++m) {
-        if (m < nv) {
-          uint32_t xp[16];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            uint4 v = xq[(m * 4 + q) * Kc + c];
-            xp[4 * q] = v.x; xp[4 * q + 1] = v.y; xp[4 * q + 2] = v.z; xp[4 * q + 3] = v.w;
-          }
-          const float xs = sums[m * Kc + c];
-#pragma unroll
-          for (int r = 0; r < RPW; ++r) {
-            float d = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) d = dot2_bf16(pr[r][i], xp[i], d);
-            acc[r][m] = fmaf(sc[r], d, acc[r][m]);
-            accz[r][m] = fmaf(zc[r], xs, accz[r][m]);
-          }
-        }
-      }
-    } else {
-      const float4 *xq = reinterpret_cast<const float4 *>(lds);
-      const float *sums = reinterpret_cast<const float *>(lds + static_cast<size_t>(MVtot) * Kc * 128);
-      if constexpr (MV == 1) {
-        // one x vector: keep it in registers, convert one row's codes at a time
-        float xf[32];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          float4 v = xq[q * Kc + c];
-          xf[4 * q] = v.x; xf[4 * q + 1] = v.y; xf[4 * q + 2] = v.z; xf[4 * q + 3] = v.w;
-        }
-        const float xs = sums[c];
-#pragma unroll
-        for (int r = 0; r < RPW; ++r) {
-          float d0 = 0.0f, d1 = 0.0f;
-          static_for<0, 16>([&](auto h) {
-            constexpr int k = 2 * decltype(h)::value;
-            d0 = fmaf(code_f32<BITS, k>(st.w[r]), xf[k], d0);
-            d1 = fmaf(code_f32<BITS, k + 1>(st.w[r]), xf[k + 1], d1);
-          });
-          acc[r][0] = fmaf(bf16_to_f32(st.s[r]), d0 + d1, fmaf(bf16_to_f32(st.b[r]), xs, acc[r][0]));
-        }
-      } else {
-        float qf[RPW][32];
-#pragma unroll
-        for (int r = 0; r < RPW; ++r)
-          static_for<0, 32>([&](auto k) { qf[r][decltype(k)::value] = code_f32<BITS, decltype(k)::value>(st.w[r]); });
-#pragma unroll
-        for (int m = 0; m < MV; ++m) {
-          if (m < nv) {
-            float xf[32];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-              float4 v = xq[(m * 8 + q) * Kc + c];
-              xf[4 * q] = v.x; xf[4 * q + 1] = v.y; xf[4 * q + 2] = v.z; xf[4 * q + 3] = v.w;
-            }
-            const float xs = sums[m * Kc + c];
-#pragma unroll
-            for (int r = 0; r < RPW; ++r) {
-              float d0 = 0.0f, d1 = 0.0f;
-#pragma unroll
-              for (int k = 0; k < 32; k += 2) {
-                d0 = fmaf(qf[r][k], xf[k], d0);
-                d1 = fmaf(qf[r][k + 1], xf[k + 1], d1);
-              }
-              acc[r][m] = fmaf(bf16_to_f32(st.s[r]), d0 + d1, fmaf(bf16_to_f32(st.b[r]), xs, acc[r][m]));
-            }
-          }
-        }
-      }
-    }
+    accumulate_chunk<BITS, RPW, MV, PAIR>(st, lds, nv, c, pk, acc, accz);
   }
 
   // Issue the first two steps' loads (before x staging); with one step the
@@ -310,12 +334,12 @@ struct WaveEngine {
     load(1, B);
   }
 
-  __device__ __forceinline__ void run(const unsigned char *lds, int MVtot, int nv) {
+  __device__ __forceinline__ void run(const unsigned char *lds, int nv) {
     for (int step = 0; step < nsteps; step += 2) {
-      compute(step, A, lds, MVtot, nv);
+      compute(step, A, lds, nv);
       if (step + 2 < nsteps) load(step + 2, A);
       if (step + 1 < nsteps) {
-        compute(step + 1, B, lds, MVtot, nv);
+        compute(step + 1, B, lds, nv);
         if (step + 3 < nsteps) load(step + 3, B);
       }
     }
@@ -380,11 +404,11 @@ __global__ __launch_bounds__(kBlock) void qmv_kernel(QmvArgs a) {
   };
   auto stage_item = [&](int it) {
     if constexpr (XIN == XIN_SILU) {
-      stage_silu_raw(raw0, raw1, smem, Kc, it);
+      stage_silu_raw(raw0, raw1, smem, it);
     } else {
       const int m = it / Kc, c = it - m * Kc;
-      if constexpr (PAIR) stage_pairs_raw<BITS>(raw0, smem, Kc, MV, m, c);
-      else stage_f32_raw(raw0, smem, Kc, MV, m, c);
+      if constexpr (PAIR) stage_pairs_raw<BITS, MV>(raw0, smem, m, c);
+      else stage_f32_raw<MV>(raw0, smem, m, c);
     }
   };
   // First item: an unconditional (clamped) load issued before the weight
@@ -401,7 +425,7 @@ __global__ __launch_bounds__(kBlock) void qmv_kernel(QmvArgs a) {
   }
   __syncthreads();
 
-  eng.run(smem, (XIN == XIN_SILU) ? 1 : MV, a.M);
+  eng.run(smem, a.M);
 
   constexpr int V = pow2_ceil(RPW * MV);
   float vals[V];
@@ -433,11 +457,20 @@ __global__ __launch_bounds__(kBlock) void qmv_kernel(QmvArgs a) {
 
 // ----------------------------------------------------------------------------
 // Gather kernel (mlx.core.gather_qmm; quantized.h adjust_matrix_offsets):
-// y[p] = x[lhs[p]] @ W[rhs[p]]^T.  Workgroup (e, tile) serves every pair p
-// with rhs[p] == e: it reads tile rows of expert e's W ONCE for all of them
-// (x vectors batched MV at a time).  The pairs of e are found in order of p,
-// by a scan of rhs (any order) or by binary search when rhs is sorted, so
-// both modes run the same arithmetic for every output.
+// y[p] = x[lhs[p]] @ W[rhs[p]]^T.
+//
+// Workgroup (e, tile) owns `tile_rows` consecutive rows of expert e and
+// serves every pair p with rhs[p] == e, so each row of an expert's weight is
+// read once for all the tokens routed to it (up to MV x vectors at a time).
+// The pairs of e are found by a block-wide ordered scan of rhs (ballot +
+// per-wave counts): the list is in increasing p whatever the order of rhs,
+// so sorted and unsorted indices run identical arithmetic for every output.
+// Lists longer than kGatherListMax are processed in windows.
+//
+// Each wave streams its share of the tile (row groups of RPW rows) through a
+// DEPTH-deep software pipeline that runs across row groups; loads are
+// branch-free (clamped), and a row group's partial sums are reduced and
+// stored as soon as its last chunk is in.
 // ----------------------------------------------------------------------------
 struct GatherArgs {
   const uint16_t *x;        // [Bx, M, K]
@@ -450,113 +483,144 @@ struct GatherArgs {
   int M;
   int gshift;
   int tiles;                // row tiles per expert
-  int sorted;
+  int tile_rows;            // rows per tile (a multiple of waves * RPW)
   int out_f32;
   void *y;                  // [P, M, N]
 };
 
-constexpr int kGatherListMax = 1024;   // pairs of one expert handled per pass
+constexpr int kGatherListMax = 1024;   // pairs of one expert per window
 
-template <int BITS, int RPW, int MV>
-__global__ __launch_bounds__(kBlock) void gather_kernel(GatherArgs a) {
+template <int BITS, int RPW, int MV, int GW, int DEPTH>
+__global__ __launch_bounds__(GW * kWave) void gather_kernel(GatherArgs a) {
   constexpr bool PAIR = BITS <= 6;
+  constexpr int NT = GW * kWave;
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int list[kGatherListMax];
-  __shared__ int list_n;
-  __shared__ int list_base;
+  __shared__ int wcnt[GW];
+
   const int e = blockIdx.x / a.tiles;
   const int tile = blockIdx.x - e * a.tiles;
   const int lane = threadIdx.x & (kWave - 1);
-  // wave index, made visibly wave-uniform so row pointers live in SGPRs
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int Kc = a.K >> 5;
-  const int64_t wstride = static_cast<int64_t>(Kc) * BITS;
-  const int64_t gstride = Kc >> a.gshift;
-  const int64_t row0 = (static_cast<int64_t>(tile) * kWavesPerBlock + wid) * RPW;
-
-  // ---- the ordered list of pairs routed to expert e
-  if (a.sorted) {
-    if (threadIdx.x == 0) {
-      int64_t lo = 0, hi = a.P;
-      while (lo < hi) { int64_t mid = (lo + hi) >> 1; if (a.rhs[mid] < static_cast<uint32_t>(e)) lo = mid + 1; else hi = mid; }
-      int64_t lo2 = lo, hi2 = a.P;
-      while (lo2 < hi2) { int64_t mid = (lo2 + hi2) >> 1; if (a.rhs[mid] <= static_cast<uint32_t>(e)) lo2 = mid + 1; else hi2 = mid; }
-      list_base = static_cast<int>(lo);
-      list_n = static_cast<int>(lo2 - lo);
-    }
-    __syncthreads();
-  } else {
-    if (wid == 0) {
-      int n = 0;
-      for (int64_t p0 = 0; p0 < a.P; p0 += kWave) {
-        const int64_t p = p0 + lane;
-        const bool hit = p < a.P && a.rhs[p] == static_cast<uint32_t>(e);
-        const unsigned long long mask = __ballot(hit);
-        const int before = __popcll(mask & ((1ull << lane) - 1ull));
-        if (hit && n + before < kGatherListMax) list[n + before] = static_cast<int>(p);
-        n += __popcll(mask);
-      }
-      if (lane == 0) { list_n = n; list_base = -1; }
-    }
-    __syncthreads();
-  }
-  const int npairs = list_n;
-  if (npairs == 0) return;   // uniform across the workgroup
-  const int base = list_base;
-  const int nvec_total = npairs * a.M;
-
+  const int nsteps = (Kc + kWave - 1) / kWave;
+  const int64_t wstride = static_cast<int64_t>(Kc) * BITS;   // words per row
+  const int64_t gstride = Kc >> a.gshift;                    // groups per row
+  const int64_t row_base = static_cast<int64_t>(tile) * a.tile_rows + wid * RPW;
+  const int RG = a.tile_rows / (GW * RPW);
+  const int T = RG * nsteps;
   const uint32_t *we = a.w + static_cast<int64_t>(e) * a.N * wstride;
   const uint16_t *se = a.s + static_cast<int64_t>(e) * a.N * gstride;
   const uint16_t *be = a.b + static_cast<int64_t>(e) * a.N * gstride;
+  const PairConsts pk = pair_consts<BITS>();
 
-  for (int v0 = 0; v0 < nvec_total; v0 += MV) {
-    const int nv = min(MV, nvec_total - v0);
-    WaveEngine<BITS, RPW, MV, PAIR> eng;
-    eng.init(Kc, a.gshift, lane);
+  auto row_of = [&](int rg, int r) -> int64_t {
+    const int64_t row = row_base + static_cast<int64_t>(rg) * (GW * RPW) + r;
+    return row < a.N - 1 ? row : a.N - 1;
+  };
+  auto load = [&](int t, ChunkStep<BITS, RPW> &st) {
+    t = t < T - 1 ? t : T - 1;                         // clamped: branch-free
+    const int rg = t / nsteps, step = t - rg * nsteps;
+    const uint32_t c = static_cast<uint32_t>(min(step * kWave + lane, Kc - 1));
+    const uint32_t gi = c >> a.gshift;
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
-      int64_t gr = row0 + r;
-      if (gr > a.N - 1) gr = a.N - 1;
-      eng.wrow[r] = we + gr * wstride;
-      eng.srow[r] = se + gr * gstride;
-      eng.brow[r] = be + gr * gstride;
+      const int64_t row = uniform_index(row_of(rg, r));
+      load_chunk<BITS>(byte_offset(we + row * wstride, c * (BITS * 4)), st.w[r]);
+      st.s[r] = *byte_offset(se + row * gstride, gi * 2);
+      st.b[r] = *byte_offset(be + row * gstride, gi * 2);
     }
-    eng.prefetch();
-    for (int it = threadIdx.x; it < nv * Kc; it += kBlock) {
-      const int mv = it / Kc, c = it - mv * Kc;
-      const int vec = v0 + mv;
-      const int pi = vec / a.M, m = vec - pi * a.M;
-      const int p = base >= 0 ? base + pi : (pi < kGatherListMax ? list[pi] : 0);
-      const uint16_t *xk = a.x + (static_cast<int64_t>(a.lhs[p]) * a.M + m) * a.K + static_cast<int64_t>(c) * 32;
-      if constexpr (PAIR) stage_pairs_chunk<BITS>(xk, smem, Kc, MV, mv, c);
-      else stage_f32_chunk(xk, smem, Kc, MV, mv, c);
-    }
-    __syncthreads();
-    eng.run(smem, MV, nv);
+  };
 
-    constexpr int V = pow2_ceil(RPW * MV);
-    float vals[V];
+  for (int win = 0;; win += kGatherListMax) {
+    // ---- ordered list of the pairs routed to e, ranks [win, win + max)
+    int seen = 0;
+    for (int64_t p0 = 0; p0 < a.P; p0 += NT) {
+      const int64_t p = p0 + threadIdx.x;
+      const bool hit = p < a.P && a.rhs[p] == static_cast<uint32_t>(e);
+      const unsigned long long mask = __ballot(hit);
+      if (lane == 0) wcnt[wid] = __popcll(mask);
+      __syncthreads();
+      int before = seen + __popcll(mask & ((1ull << lane) - 1ull));
+      int round = 0;
 #pragma unroll
-    for (int i = 0; i < V; ++i) vals[i] = 0.0f;
-#pragma unroll
-    for (int r = 0; r < RPW; ++r)
-#pragma unroll
-      for (int m = 0; m < MV; ++m) vals[r * MV + m] = eng.result(r, m);
-    const float tot = wave_reduce_many<V>(vals, lane);
-    if (reduce_leader<V>(lane)) {
-      const int idx = reduce_index<V>(lane);
-      const int r = idx / MV, mv = idx % MV;
-      const int64_t gr = row0 + r;
-      if (idx < RPW * MV && mv < nv && gr < a.N) {
+      for (int w = 0; w < GW; ++w) {
+        const int cnt = wcnt[w];
+        before += (w < wid) ? cnt : 0;
+        round += cnt;
+      }
+      if (hit && before >= win && before < win + kGatherListMax) list[before - win] = static_cast<int>(p);
+      seen += round;
+      __syncthreads();
+    }
+    const int npairs = min(seen - win, kGatherListMax);
+    if (npairs <= 0) return;                           // uniform
+    const int nvec = npairs * a.M;
+
+    for (int v0 = 0; v0 < nvec; v0 += MV) {
+      const int nv = min(MV, nvec - v0);
+      ChunkStep<BITS, RPW> ring[DEPTH];
+      static_for<0, DEPTH>([&](auto d) { load(decltype(d)::value, ring[decltype(d)::value]); });
+      // stage this slab's x vectors
+      for (int it = threadIdx.x; it < nv * Kc; it += NT) {
+        const int mv = it / Kc, c = it - mv * Kc;
         const int vec = v0 + mv;
         const int pi = vec / a.M, m = vec - pi * a.M;
-        const int p = base >= 0 ? base + pi : list[pi];
-        const int64_t o = (static_cast<int64_t>(p) * a.M + m) * a.N + gr;
-        if (a.out_f32) static_cast<float *>(a.y)[o] = tot;
-        else static_cast<uint16_t *>(a.y)[o] = f32_to_bf16(tot);
+        const int p = list[pi];
+        const uint16_t *xk = a.x + (static_cast<int64_t>(a.lhs[p]) * a.M + m) * a.K + static_cast<int64_t>(c) * 32;
+        if constexpr (PAIR) stage_pairs_chunk<BITS, MV>(xk, smem, mv, c);
+        else stage_f32_chunk<MV>(xk, smem, mv, c);
       }
+      __syncthreads();
+
+      float acc[RPW][MV], accz[RPW][MV];
+#pragma unroll
+      for (int r = 0; r < RPW; ++r)
+#pragma unroll
+        for (int m = 0; m < MV; ++m) acc[r][m] = accz[r][m] = 0.0f;
+
+      auto consume = [&](int t, const ChunkStep<BITS, RPW> &st) {
+        const int rg = t / nsteps, step = t - rg * nsteps;
+        const int c = step * kWave + lane;
+        if (c < Kc) accumulate_chunk<BITS, RPW, MV, PAIR>(st, smem, nv, c, pk, acc, accz);
+        if (step == nsteps - 1) {                        // row group complete
+          constexpr int V = pow2_ceil(RPW * MV);
+          float vals[V];
+#pragma unroll
+          for (int i = 0; i < V; ++i) vals[i] = 0.0f;
+#pragma unroll
+          for (int r = 0; r < RPW; ++r)
+#pragma unroll
+            for (int m = 0; m < MV; ++m) {
+              vals[r * MV + m] = PAIR ? fmaf(acc[r][m], 1.0f / static_cast<float>(1 << PairPlan<BITS>::P), accz[r][m])
+                                      : acc[r][m];
+              acc[r][m] = accz[r][m] = 0.0f;
+            }
+          const float tot = wave_reduce_many<V>(vals, lane);
+          if (reduce_leader<V>(lane)) {
+            const int idx = reduce_index<V>(lane);
+            const int r = idx / MV, mv = idx - r * MV;
+            const int64_t row = row_base + static_cast<int64_t>(rg) * (GW * RPW) + r;
+            if (idx < RPW * MV && mv < nv && row < a.N) {
+              const int vec = v0 + mv;
+              const int pi = vec / a.M, m = vec - pi * a.M;
+              const int64_t o = (static_cast<int64_t>(list[pi]) * a.M + m) * a.N + row;
+              if (a.out_f32) static_cast<float *>(a.y)[o] = tot;
+              else static_cast<uint16_t *>(a.y)[o] = f32_to_bf16(tot);
+            }
+          }
+        }
+      };
+      for (int t = 0; t < T; t += DEPTH) {
+        static_for<0, DEPTH>([&](auto d) {
+          constexpr int dd = decltype(d)::value;
+          if (t + dd < T) consume(t + dd, ring[dd]);
+          load(t + dd + DEPTH, ring[dd]);
+        });
+      }
+      __syncthreads();   // LDS and list reuse by the next slab / window
     }
-    __syncthreads();   // LDS reuse by the next batch of vectors
+    if (seen <= win + kGatherListMax) return;
   }
 }
 
