@@ -96,9 +96,6 @@ def test_gather_rejects_bad_arguments():
     # transpose=0 not implemented
     assert L.gather_qmv(*base, FAKE, FAKE, 8, *tail, 0, 0, 0, None) == \
         q.QMV_EUNSUPPORTED
-    # unsorted beyond the in-kernel list capacity
-    assert L.gather_qmv(*base, FAKE, FAKE, 5000, *tail, 1, 0, 0, None) == \
-        q.QMV_EUNSUPPORTED
 
 
 def test_unpack_rejects_bad_arguments():

@@ -324,6 +324,26 @@ def test_gather_small(dev, bits, M):
         _run_gather(dev, x, ew, lhs[perm], rhs[perm], g, bits, True), y[perm])
 
 
+@pytest.mark.parametrize("sorted_indices", (False, True))
+def test_gather_long_pair_lists(dev, sorted_indices):
+    """2500 pairs over 3 experts: one expert's list exceeds the 1024-pair
+    routing window, so its rows are served in several windows."""
+    E, N, K, g, bits = 3, 48, 256, 64, 4
+    ew = _experts(E, N, K, bits, g, seed0=77)
+    rng = np.random.default_rng(5)
+    Bx, P = 40, 2500
+    x = synth.activation_bf16((Bx, 1, K), seed=6)
+    lhs = rng.integers(0, Bx, P).astype(np.uint32)
+    rhs = rng.choice(E, P, p=[0.7, 0.2, 0.1]).astype(np.uint32)
+    if sorted_indices:
+        perm = np.argsort(rhs, kind="stable")
+        lhs, rhs = lhs[perm], rhs[perm]
+    ref = oracle.gather_qmv(x, *ew, lhs, rhs, g, bits)
+    check_t1(_run_gather(dev, x, ew, lhs, rhs, g, bits, sorted_indices), ref)
+    check_t2(_run_gather(dev, x, ew, lhs, rhs, g, bits, sorted_indices, True),
+             ref)
+
+
 def test_gather_without_indices_is_qmv(dev):
     N, K, g, bits = 300, 2048, 64, 4
     w, ow, os_, ob = packed(N, K, bits, g, seed=12)
