@@ -19,6 +19,8 @@ outputs, each counted once per step.
 Other modes (profiling aids):
   --no-cpu-baseline   skip the CPU oracle timing
   --copy-calibration  run a plain 256 MiB device copy (counter scaling)
+  --copy-reference    time a plain device copy of the workload's byte count
+  --eager             time host-launched steps instead of a graph replay
 """
 from __future__ import annotations
 
@@ -383,6 +385,29 @@ def copy_calibration(steps: int):
                       "copy_calibration_bytes_written": n, "launches": steps}))
 
 
+def copy_reference(nbytes: int, steps: int):
+    """A plain device copy of `nbytes` (read + write), rotated over >= 512 MB
+    and timed like the workloads: what a streaming kernel of this size
+    achieves on this machine, for context beside the roofline."""
+    import torch
+    n = (nbytes // 4096) * 4096
+    sets = max(2, math.ceil(ROTATE_BYTES / (2 * n)))
+    bufs = [(torch.ones(n, dtype=torch.uint8, device="cuda"),
+             torch.empty(n, dtype=torch.uint8, device="cuda"))
+            for _ in range(sets)]
+    torch.cuda.synchronize()
+
+    def step(i, stream):
+        a, b = bufs[i % sets]
+        b.copy_(a)
+    for i in range(20):
+        step(i, None)
+    ms = _time_graph(step, steps, 0)
+    return {"copy_bytes": n, "ms_per_copy": round(ms, 6),
+            "read_plus_write_GBs": round(2 * n / (ms * 1e-3) / 1e9, 1),
+            "frac_of_8TBs": round(2 * n / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -393,6 +418,8 @@ def main():
     ap.add_argument("--list", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--copy-reference", action="store_true",
+                    help="time a plain device copy of the workload's size")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches instead of a graph replay")
     args = ap.parse_args()
@@ -412,6 +439,11 @@ def main():
         copy_calibration(args.steps)
         return
     import synth
+    if args.copy_reference:
+        n = args.workload or synth.HEADLINE["name"]
+        print(json.dumps({"workload": n, **copy_reference(W[n].nbytes,
+                                                          args.steps)}))
+        return
     names = list(W) if args.all else [args.workload or synth.HEADLINE["name"]]
     for n in names:
         if n not in W:
