@@ -81,20 +81,41 @@ void allow_lds(Kern kern, int64_t bytes) {
 #endif
 constexpr int kRpw = QMV_RPW;
 
+#ifndef QMV_FORCE_WPB
+#define QMV_FORCE_WPB 0   // 4 or 8 forces the waves per workgroup; 0 chooses by LDS
+#endif
+
+template <int BITS, int MV, int XIN, int WPB>
+int launch_qmv_wpb(const qmvk::QmvArgs &a, int64_t lds, hipStream_t st) {
+  const int64_t rows = static_cast<int64_t>(a.nmat) * a.N;
+  const int64_t rows_per_block = WPB * kRpw;
+  const int64_t blocks = (rows + rows_per_block - 1) / rows_per_block;
+  if (blocks > 0x7FFFFFFF) return fail(QMV_EUNSUPPORTED, "qmv: too many rows");
+  auto kern = qmvk::qmv_kernel<BITS, kRpw, MV, XIN, WPB>;
+  allow_lds(kern, lds);
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(WPB * qmvk::kWave),
+                     static_cast<size_t>(lds), st, a);
+  return check_launch("qmv");
+}
+
+// Every workgroup stages the whole of x in LDS, so with a large K (or several
+// vectors) few workgroups fit on a CU.  8-wave workgroups then keep more of
+// the CU's wave slots filled and give more threads to the staging (measured
+// on MI355X: 4096x14336 silu tail 17.2 -> 15.0 us, 4 vectors at 4096x4096
+// 6.6 -> 6.0 us; 16-wave workgroups were slower everywhere).
+int qmv_waves_per_block(int64_t lds) {
+  if (QMV_FORCE_WPB) return QMV_FORCE_WPB;
+  const int64_t per_cu = lds > 0 ? kMaxLds / lds : 32;
+  return per_cu * 4 >= 32 ? 4 : 8;
+}
+
 template <int BITS, int MV, int XIN>
 int launch_qmv_t(const qmvk::QmvArgs &a, hipStream_t st) {
   constexpr bool PAIR = (BITS <= 6) && (XIN == qmvk::XIN_PLAIN);
   const int64_t Kc = a.K / 32;
   const int64_t lds = Kc * qmvk::chunk_stride<PAIR, (XIN == qmvk::XIN_SILU ? 1 : MV)>();
-  const int64_t rows = static_cast<int64_t>(a.nmat) * a.N;
-  const int64_t rows_per_block = qmvk::kWavesPerBlock * kRpw;
-  const int64_t blocks = (rows + rows_per_block - 1) / rows_per_block;
-  if (blocks > 0x7FFFFFFF) return fail(QMV_EUNSUPPORTED, "qmv: too many rows");
-  auto kern = qmvk::qmv_kernel<BITS, kRpw, MV, XIN>;
-  allow_lds(kern, lds);
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(qmvk::kBlock),
-                     static_cast<size_t>(lds), st, a);
-  return check_launch("qmv");
+  if (qmv_waves_per_block(lds) == 4) return launch_qmv_wpb<BITS, MV, XIN, 4>(a, lds, st);
+  return launch_qmv_wpb<BITS, MV, XIN, 8>(a, lds, st);
 }
 
 template <int MV, int XIN>
@@ -117,41 +138,56 @@ int64_t qmv_lds_bytes(int bits, int mv, int64_t K) {
 
 // ------------------------------------------------------------------ gather
 #ifndef QMV_GATHER_WAVES
-#define QMV_GATHER_WAVES 8
+#define QMV_GATHER_WAVES 4
 #endif
 #ifndef QMV_GATHER_DEPTH
 #define QMV_GATHER_DEPTH 4
 #endif
 #ifndef QMV_GATHER_RPW
-#define QMV_GATHER_RPW 2
+#define QMV_GATHER_RPW 1
+#endif
+#ifndef QMV_GATHER_TILES
+#define QMV_GATHER_TILES 2048     // target workgroups over the whole expert stack
 #endif
 constexpr int kGatherRpw = QMV_GATHER_RPW;
+constexpr int64_t kGatherTiles = QMV_GATHER_TILES;
 constexpr int kGatherWaves = QMV_GATHER_WAVES;
 constexpr int kGatherDepth = QMV_GATHER_DEPTH;   // chunk steps in flight per wave
 // x vectors per pass over an expert's rows (fp32 staging is twice as wide)
 template <int BITS>
 constexpr int gather_mv() { return BITS <= 6 ? 4 : 2; }
+// static LDS of the gather kernel: pair list, x rows, per-wave counts
+constexpr int64_t kGatherStaticLds = 2 * 4 * qmvk::kGatherListMax + 4 * kGatherWaves;
 
 template <int BITS>
 int launch_gather_t(const qmvk::GatherArgs &a0, int64_t E, hipStream_t st) {
   constexpr int kGatherMv = gather_mv<BITS>();
   qmvk::GatherArgs a = a0;
   const int64_t Kc = a.K / 32;
-  const int64_t lds = Kc * qmvk::chunk_stride<(BITS <= 6), kGatherMv>();
-  // Tiles of `tile_rows` rows: large enough that routing and x staging are
-  // paid once per many rows, small enough for ~2 workgroups per CU over the
-  // expert stack.
+  const int64_t lds_x = Kc * qmvk::chunk_stride<(BITS <= 6), kGatherMv>();
+  // Tiles of `tile_rows` rows: many small workgroups (~8 per CU over the
+  // expert stack), so that most of the weight stream is in flight at once,
+  // yet enough rows per tile that routing and x staging are paid once per
+  // many rows; the parked row sums (tile_rows * MV floats) must fit in LDS
+  // beside x and the pair list.  (64x2048x2048 4-bit, 128 pairs on MI355X:
+  // 512 tiles of 2-row waves 67 us, 2048 tiles of 1-row waves 45 us.)
   const int64_t unit = kGatherWaves * kGatherRpw;
-  int64_t tile_rows = (a.N * E + 511) / 512;
+  int64_t tile_rows = (a.N * E + kGatherTiles - 1) / kGatherTiles;
   tile_rows = ((tile_rows + unit - 1) / unit) * unit;
   const int64_t n_round = ((a.N + unit - 1) / unit) * unit;
   if (tile_rows > n_round) tile_rows = n_round;
   if (tile_rows > 4096) tile_rows = 4096;
   if (tile_rows < unit) tile_rows = unit;
+  const int64_t lds_budget = kMaxLds - kGatherStaticLds;
+  while (tile_rows > unit && lds_x + tile_rows * kGatherMv * 4 > lds_budget)
+    tile_rows = ((tile_rows / 2 + unit - 1) / unit) * unit;
+  const int64_t lds = lds_x + tile_rows * kGatherMv * 4;
+  if (lds > lds_budget) return fail(QMV_EUNSUPPORTED, "gather_qmv: K=%lld too large", (long long)a.K);
   const int64_t tiles = (a.N + tile_rows - 1) / tile_rows;
   if (E * tiles > 0x7FFFFFFF) return fail(QMV_EUNSUPPORTED, "gather_qmv: grid too large");
   a.tiles = static_cast<int>(tiles);
   a.tile_rows = static_cast<int>(tile_rows);
+  a.res_offset = static_cast<int>(lds_x);
   auto kern = qmvk::gather_kernel<BITS, kGatherRpw, kGatherMv, kGatherWaves, kGatherDepth>;
   allow_lds(kern, lds);
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(E * tiles)), dim3(kGatherWaves * qmvk::kWave),
@@ -328,7 +364,7 @@ int gather_qmv(const uint16_t *x, int64_t Bx, const uint32_t *w_q, const uint16_
   if (P <= 0) return fail(QMV_EINVAL, "gather_qmv: P=%lld must be positive", (long long)P);
   if (int rc = check_aligned("gather_qmv", x, "x")) return rc;
   if (int rc = check_aligned("gather_qmv", w_q, "w_q")) return rc;
-  if (qmv_lds_bytes(bits, bits <= 6 ? gather_mv<4>() : gather_mv<8>(), K) > kMaxLds)
+  if (qmv_lds_bytes(bits, bits <= 6 ? gather_mv<4>() : gather_mv<8>(), K) > kMaxLds - kGatherStaticLds)
     return fail(QMV_EUNSUPPORTED, "gather_qmv: K=%lld too large", (long long)K);
   if (M > (int64_t(1) << 20) || P > (int64_t(1) << 30))
     return fail(QMV_EUNSUPPORTED, "gather_qmv: M or P too large");
@@ -341,6 +377,7 @@ int gather_qmv(const uint16_t *x, int64_t Bx, const uint32_t *w_q, const uint16_
   a.rhs = rhs_indices;
   a.P = P;
   a.N = N;
+  a.Bx = Bx;
   a.K = static_cast<int>(K);
   a.M = static_cast<int>(M);
   a.gshift = gshift_of(group_size);

@@ -33,16 +33,11 @@
 namespace qmvk {
 
 // Build-time tuning knobs (defaults are the measured best on MI355X).
-#ifndef QMV_WAVES_PER_BLOCK
-#define QMV_WAVES_PER_BLOCK 4
-#endif
 #ifndef QMV_NT_LOADS
 #define QMV_NT_LOADS 1
 #endif
 
 constexpr int kWave = 64;
-constexpr int kWavesPerBlock = QMV_WAVES_PER_BLOCK;
-constexpr int kBlock = kWave * kWavesPerBlock;
 constexpr uint32_t kMagic2 = 0x43004300u;   // two bf16 values of 128.0
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));

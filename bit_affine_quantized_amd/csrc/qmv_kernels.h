@@ -348,7 +348,10 @@ struct WaveEngine {
 
 // ----------------------------------------------------------------------------
 // qmv / gate_up / silu-tail kernel.  Rows of `nmat` matrices (same N, K, bits,
-// group size) are concatenated; wave w of block b owns rows (4b + w)*RPW...
+// group size) are concatenated; wave w of block b owns rows (WPB b + w)*RPW...
+// The whole grid is normally resident at once, so every wave's weight loads
+// are issued at the start (a streaming grid that walks rows with a bounded
+// number of loads in flight measured far slower on MI355X).
 // ----------------------------------------------------------------------------
 enum { XIN_PLAIN = 0, XIN_SILU = 1 };
 
@@ -366,8 +369,9 @@ struct QmvArgs {
   int64_t y_ld;           // stride between output vectors (elements)
 };
 
-template <int BITS, int RPW, int MV, int XIN>
-__global__ __launch_bounds__(kBlock) void qmv_kernel(QmvArgs a) {
+template <int BITS, int RPW, int MV, int XIN, int WPB>
+__global__ __launch_bounds__(WPB * kWave) void qmv_kernel(QmvArgs a) {
+  constexpr int kBlock = WPB * kWave;
   constexpr bool PAIR = (BITS <= 6) && (XIN == XIN_PLAIN);
   extern __shared__ __align__(16) unsigned char smem[];
   const int Kc = a.K >> 5;
@@ -375,7 +379,7 @@ __global__ __launch_bounds__(kBlock) void qmv_kernel(QmvArgs a) {
   // wave index, made visibly wave-uniform so row pointers live in SGPRs
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int64_t total = static_cast<int64_t>(a.nmat) * a.N;
-  const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wid) * RPW;
+  const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * WPB + wid) * RPW;
   const int64_t wstride = static_cast<int64_t>(Kc) * BITS;
   const int64_t gstride = Kc >> a.gshift;
 
@@ -406,7 +410,8 @@ __global__ __launch_bounds__(kBlock) void qmv_kernel(QmvArgs a) {
     if constexpr (XIN == XIN_SILU) {
       stage_silu_raw(raw0, raw1, smem, it);
     } else {
-      const int m = it / Kc, c = it - m * Kc;
+      // one-vector launches (MV == 1) skip the division: it costs ~30 VALU
+      const int m = (MV == 1) ? 0 : it / Kc, c = it - m * Kc;
       if constexpr (PAIR) stage_pairs_raw<BITS, MV>(raw0, smem, m, c);
       else stage_f32_raw<MV>(raw0, smem, m, c);
     }
@@ -479,11 +484,13 @@ struct GatherArgs {
   const uint32_t *lhs, *rhs;
   int64_t P;
   int64_t N;
+  int64_t Bx;
   int K;
   int M;
   int gshift;
   int tiles;                // row tiles per expert
   int tile_rows;            // rows per tile (a multiple of waves * RPW)
+  int res_offset;           // LDS bytes before the parked row sums
   int out_f32;
   void *y;                  // [P, M, N]
 };
@@ -495,7 +502,8 @@ __global__ __launch_bounds__(GW * kWave) void gather_kernel(GatherArgs a) {
   constexpr bool PAIR = BITS <= 6;
   constexpr int NT = GW * kWave;
   extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ int list[kGatherListMax];
+  __shared__ int list[kGatherListMax];    // pair index p, in increasing order
+  __shared__ int xrow[kGatherListMax];    // its x batch row lhs[p]
   __shared__ int wcnt[GW];
 
   const int e = blockIdx.x / a.tiles;
@@ -513,24 +521,66 @@ __global__ __launch_bounds__(GW * kWave) void gather_kernel(GatherArgs a) {
   const uint16_t *se = a.s + static_cast<int64_t>(e) * a.N * gstride;
   const uint16_t *be = a.b + static_cast<int64_t>(e) * a.N * gstride;
   const PairConsts pk = pair_consts<BITS>();
+  // Row sums are parked in LDS (RG * RPW * MV floats per wave) and written
+  // out after the row loop: global stores inside it would share the memory
+  // counter with the weight loads and force full waits on every step.
+  float *res = reinterpret_cast<float *>(smem + a.res_offset) + wid * (RG * RPW * MV);
 
-  auto row_of = [&](int rg, int r) -> int64_t {
-    const int64_t row = row_base + static_cast<int64_t>(rg) * (GW * RPW) + r;
-    return row < a.N - 1 ? row : a.N - 1;
-  };
-  auto load = [&](int t, ChunkStep<BITS, RPW> &st) {
-    t = t < T - 1 ? t : T - 1;                         // clamped: branch-free
-    const int rg = t / nsteps, step = t - rg * nsteps;
-    const uint32_t c = static_cast<uint32_t>(min(step * kWave + lane, Kc - 1));
+  // ---- the weight stream: RG row groups x nsteps chunk steps per wave, with
+  // DEPTH steps in flight.  Scalar cursors point at the current row group's
+  // first row and advance by GW*RPW rows; rows past N and steps past the
+  // wave's last read the (hot) head of x instead and are never consumed.
+  const uint32_t dummy_off = static_cast<uint32_t>(min(lane * 16, a.K * 2 - 32));
+  const int64_t wrow_bytes = wstride * 4, grow_bytes = gstride * 2;
+  const int64_t left0 = a.N - row_base;
+  const int rows_left0 = static_cast<int>(left0 < 0x40000000 ? left0 : 0x40000000);
+  const unsigned char *w0 = reinterpret_cast<const unsigned char *>(we) + row_base * wrow_bytes;
+  const unsigned char *s0 = reinterpret_cast<const unsigned char *>(se) + row_base * grow_bytes;
+  const unsigned char *b0 = reinterpret_cast<const unsigned char *>(be) + row_base * grow_bytes;
+  const unsigned char *wcur = w0, *scur = s0, *bcur = b0;
+  int l_t = 0, l_step = 0, rows_left = rows_left0;
+  auto load_next = [&](ChunkStep<BITS, RPW> &st) {
+    const bool live = l_t < T;
+    const uint32_t c = static_cast<uint32_t>(min(l_step * kWave + lane, Kc - 1));
     const uint32_t gi = c >> a.gshift;
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
-      const int64_t row = uniform_index(row_of(rg, r));
-      load_chunk<BITS>(byte_offset(we + row * wstride, c * (BITS * 4)), st.w[r]);
-      st.s[r] = *byte_offset(se + row * gstride, gi * 2);
-      st.b[r] = *byte_offset(be + row * gstride, gi * 2);
+      const bool ok = live && r < rows_left;
+      const unsigned char *wp = ok ? wcur + r * wrow_bytes : reinterpret_cast<const unsigned char *>(a.x);
+      const unsigned char *sp = ok ? scur + r * grow_bytes : reinterpret_cast<const unsigned char *>(a.x);
+      const unsigned char *bp = ok ? bcur + r * grow_bytes : reinterpret_cast<const unsigned char *>(a.x);
+      load_chunk<BITS>(reinterpret_cast<const uint32_t *>(wp + (ok ? c * (BITS * 4) : dummy_off)), st.w[r]);
+      st.s[r] = *reinterpret_cast<const uint16_t *>(sp + (ok ? gi * 2 : dummy_off));
+      st.b[r] = *reinterpret_cast<const uint16_t *>(bp + (ok ? gi * 2 : dummy_off));
     }
+    // advance by selects (increments in branches end up in scratch)
+    const bool wrap = l_step + 1 == nsteps;
+    l_t += 1;
+    l_step = wrap ? 0 : l_step + 1;
+    rows_left -= wrap ? GW * RPW : 0;
+    wcur += wrap ? (GW * RPW) * wrow_bytes : 0;
+    scur += wrap ? (GW * RPW) * grow_bytes : 0;
+    bcur += wrap ? (GW * RPW) * grow_bytes : 0;
   };
+  auto restart = [&] {
+    // the cursors restart from an opaque zero: otherwise the first steps'
+    // addresses are hoisted out of the slab loop into VGPR pairs
+    int zero;
+    asm volatile("s_mov_b32 %0, 0" : "=s"(zero));
+    l_t = zero;
+    l_step = zero;
+    rows_left = rows_left0 + zero;
+    wcur = w0 + zero;
+    scur = s0 + zero;
+    bcur = b0 + zero;
+  };
+  ChunkStep<BITS, RPW> ring[DEPTH];
+  // The first slab's prologue does not depend on the routing: issue it before
+  // the scan so that its latency overlaps the scan's (an expert that no pair
+  // uses wastes these few loads).
+  restart();
+  static_for<0, DEPTH>([&](auto d) { load_next(ring[decltype(d)::value]); });
+  bool primed = true;
 
   for (int win = 0;; win += kGatherListMax) {
     // ---- ordered list of the pairs routed to e, ranks [win, win + max)
@@ -549,7 +599,11 @@ __global__ __launch_bounds__(GW * kWave) void gather_kernel(GatherArgs a) {
         before += (w < wid) ? cnt : 0;
         round += cnt;
       }
-      if (hit && before >= win && before < win + kGatherListMax) list[before - win] = static_cast<int>(p);
+      if (hit && before >= win && before < win + kGatherListMax) {
+        list[before - win] = static_cast<int>(p);
+        // out-of-range rows (undefined results) are clamped: x is never overread
+        xrow[before - win] = static_cast<int>(min(static_cast<int64_t>(a.lhs[p]), a.Bx - 1));
+      }
       seen += round;
       __syncthreads();
     }
@@ -559,15 +613,20 @@ __global__ __launch_bounds__(GW * kWave) void gather_kernel(GatherArgs a) {
 
     for (int v0 = 0; v0 < nvec; v0 += MV) {
       const int nv = min(MV, nvec - v0);
-      ChunkStep<BITS, RPW> ring[DEPTH];
-      static_for<0, DEPTH>([&](auto d) { load(decltype(d)::value, ring[decltype(d)::value]); });
-      // stage this slab's x vectors
-      for (int it = threadIdx.x; it < nv * Kc; it += NT) {
+      if (!primed) {
+        restart();
+        static_for<0, DEPTH>([&](auto d) { load_next(ring[decltype(d)::value]); });
+      }
+      primed = false;
+
+      // ---- stage this slab's x vectors (issued after the weights: by the
+      // time x arrives the weight prologue has landed too)
+      const int items = nv * Kc;
+      for (int it = threadIdx.x; it < items; it += NT) {
         const int mv = it / Kc, c = it - mv * Kc;
         const int vec = v0 + mv;
         const int pi = vec / a.M, m = vec - pi * a.M;
-        const int p = list[pi];
-        const uint16_t *xk = a.x + (static_cast<int64_t>(a.lhs[p]) * a.M + m) * a.K + static_cast<int64_t>(c) * 32;
+        const uint16_t *xk = a.x + (static_cast<int64_t>(xrow[pi]) * a.M + m) * a.K + static_cast<int64_t>(c) * 32;
         if constexpr (PAIR) stage_pairs_chunk<BITS, MV>(xk, smem, mv, c);
         else stage_f32_chunk<MV>(xk, smem, mv, c);
       }
@@ -579,11 +638,12 @@ __global__ __launch_bounds__(GW * kWave) void gather_kernel(GatherArgs a) {
 #pragma unroll
         for (int m = 0; m < MV; ++m) acc[r][m] = accz[r][m] = 0.0f;
 
-      auto consume = [&](int t, const ChunkStep<BITS, RPW> &st) {
-        const int rg = t / nsteps, step = t - rg * nsteps;
-        const int c = step * kWave + lane;
+      int c_rg = 0, c_step = 0;
+      auto consume = [&](const ChunkStep<BITS, RPW> &st) {
+        const int c = c_step * kWave + lane;
         if (c < Kc) accumulate_chunk<BITS, RPW, MV, PAIR>(st, smem, nv, c, pk, acc, accz);
-        if (step == nsteps - 1) {                        // row group complete
+        const bool last = c_step == nsteps - 1;
+        if (last) {                                      // row group complete
           constexpr int V = pow2_ceil(RPW * MV);
           float vals[V];
 #pragma unroll
@@ -599,24 +659,32 @@ __global__ __launch_bounds__(GW * kWave) void gather_kernel(GatherArgs a) {
           const float tot = wave_reduce_many<V>(vals, lane);
           if (reduce_leader<V>(lane)) {
             const int idx = reduce_index<V>(lane);
-            const int r = idx / MV, mv = idx - r * MV;
-            const int64_t row = row_base + static_cast<int64_t>(rg) * (GW * RPW) + r;
-            if (idx < RPW * MV && mv < nv && row < a.N) {
-              const int vec = v0 + mv;
-              const int pi = vec / a.M, m = vec - pi * a.M;
-              const int64_t o = (static_cast<int64_t>(list[pi]) * a.M + m) * a.N + row;
-              if (a.out_f32) static_cast<float *>(a.y)[o] = tot;
-              else static_cast<uint16_t *>(a.y)[o] = f32_to_bf16(tot);
-            }
+            if (idx < RPW * MV) res[c_rg * (RPW * MV) + idx] = tot;
           }
         }
+        c_rg += last ? 1 : 0;
+        c_step = last ? 0 : c_step + 1;
       };
       for (int t = 0; t < T; t += DEPTH) {
         static_for<0, DEPTH>([&](auto d) {
           constexpr int dd = decltype(d)::value;
-          if (t + dd < T) consume(t + dd, ring[dd]);
-          load(t + dd + DEPTH, ring[dd]);
+          if (t + dd < T) consume(ring[dd]);
+          load_next(ring[dd]);
         });
+      }
+
+      // ---- write out this wave's rows (its own LDS writes, in order)
+      for (int i = lane; i < RG * RPW * MV; i += kWave) {
+        const int g = i / (RPW * MV), idx = i - g * (RPW * MV);
+        const int r = idx / MV, mv = idx - r * MV;
+        const int64_t row = row_base + static_cast<int64_t>(g) * (GW * RPW) + r;
+        if (mv < nv && row < a.N) {
+          const int vec = v0 + mv;
+          const int pi = vec / a.M, m = vec - pi * a.M;
+          const int64_t o = (static_cast<int64_t>(list[pi]) * a.M + m) * a.N + row;
+          if (a.out_f32) static_cast<float *>(a.y)[o] = res[i];
+          else static_cast<uint16_t *>(a.y)[o] = f32_to_bf16(res[i]);
+        }
       }
       __syncthreads();   // LDS and list reuse by the next slab / window
     }

@@ -34,8 +34,11 @@
  *   - bits in {2,3,4,5,6,8}; group_size in {32,64,128}; K % group_size == 0.
  *   - out_dtype QMV_OUT_BF16 rounds each output once, to nearest even;
  *     QMV_OUT_F32 writes the fp32 accumulator (a debugging mode).
- *   - Index arrays are not range-checked on the device (that needs a device
- *     read); out-of-range indices are undefined behaviour.
+ *   - Index arrays are not range-checked on the host (that needs a device
+ *     read).  Out-of-range indices give unspecified results but never read
+ *     or write outside the buffers: gather_qmv clamps an lhs index to Bx - 1,
+ *     and a pair whose rhs index is >= E is routed to no expert, so its
+ *     output rows are left unwritten.
  *   - Concurrent calls on different streams are independent.
  */
 #ifndef QMV_H
