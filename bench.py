@@ -118,6 +118,37 @@ def make_qmv(N, K, bits, g, M, name):
     return Workload(name, nbytes, setup, 1, cpu)
 
 
+def make_dequant(N, K, bits, g, name):
+    """Device dequantize to bf16 [N, K]: reads the packed weight, writes
+    2 bytes per weight."""
+    nbytes = qbytes(N, K, bits, g) + 2 * N * K
+
+    def setup(dev):
+        import torch
+        import bit_affine_quantized_amd as q
+        import synth
+        w = torch.from_numpy(synth.weight((N, K))).to(dev)
+        w_q, s, b = q.qmv_pack(w, g, bits)
+        del w
+        sets = max(2, math.ceil(ROTATE_BYTES / nbytes))
+        bufs = [(w_q.clone(), s.clone(), b.clone(),
+                 torch.empty((N, K), dtype=torch.bfloat16, device=dev))
+                for _ in range(sets)]
+
+        def step(i, stream):
+            wb, sb, bb, ob = bufs[i % sets]
+            q.qmv_dequantize(wb, sb, bb, g, bits, out=ob, stream=stream)
+        return step, sets
+
+    def cpu(budget_s):
+        import oracle
+        import synth
+        w_q, s, b = oracle.quantize_pack(synth.weight((N, K)), g, bits)
+        return lambda: oracle.dequantize(w_q, s, b, K, g, bits), \
+            f"full {N}x{K} b{bits} g{g} dequantize"
+    return Workload(name, nbytes, setup, 1, cpu)
+
+
 def make_gate_up(N, K, bits, g, name):
     nbytes = 2 * qbytes(N, K, bits, g) + 2 * K + 2 * 2 * N
 
@@ -272,6 +303,8 @@ def workloads():
         4096, 14336, 8, 64, "ffn_down_silu_resid_4096x14336_b8_g64")
     W["ffn_step_14336x4096_b8_g64"] = make_ffn(
         14336, 4096, 8, 64, "ffn_step_14336x4096_b8_g64")
+    W["dequant_14336x4096_b4_g64"] = make_dequant(14336, 4096, 4, 64,
+                                                  "dequant_14336x4096_b4_g64")
     m = synth.MOE
     for srt in (False, True):
         n = f"moe_gather_64x2048x2048_b4_g64_t16_top8_{'sorted' if srt else 'unsorted'}"

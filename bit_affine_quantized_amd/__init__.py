@@ -16,7 +16,7 @@ import os
 
 __all__ = [
     "QmvError", "lib", "qmv_pack", "qmv", "qmv_gate_up", "qmv_silu_gate_resid",
-    "gather_qmv", "qmv_unpack_codes", "QMV_OK", "QMV_EINVAL",
+    "gather_qmv", "qmv_dequantize", "qmv_unpack_codes", "QMV_OK", "QMV_EINVAL",
     "QMV_EUNSUPPORTED", "QMV_EHIP", "QMV_OUT_BF16", "QMV_OUT_F32",
 ]
 
@@ -39,6 +39,7 @@ SIGNATURES = {
                             _P],
     "gather_qmv": [_P, _I64, _P, _P, _P, _I64, _P, _P, _I64, _P, _I64, _I64,
                    _I64, _I, _I, _I, _I, _I, _P],
+    "qmv_dequantize": [_P, _P, _P, _P, _I64, _I64, _I, _I, _I, _P],
     "qmv_unpack_codes": [_P, _I64, _I64, _I, _P, _P],
 }
 
@@ -257,6 +258,23 @@ def gather_qmv(x, w_q, scales, biases, lhs_indices=None, rhs_indices=None,
           group_size, bits, 1 if transpose else 0, 1 if sorted_indices else 0,
           code, _stream(stream))
     return y
+
+
+def qmv_dequantize(w_q, scales, biases, group_size: int = 64, bits: int = 4,
+                   out_dtype=None, out=None, stream=None):
+    """W_hat [N, K] = scales * q + biases (bf16 or fp32), rounded once."""
+    torch = _torch()
+    _wq(w_q)
+    _bits16(scales, "scales")
+    _bits16(biases, "biases")
+    N = w_q.shape[0]
+    K = w_q.shape[-1] * 32 // bits
+    code, dt = _out_code(out_dtype)
+    if out is None:
+        out = torch.empty((N, K), dtype=dt, device=w_q.device)
+    _call("qmv_dequantize", _ptr(w_q), _ptr(scales), _ptr(biases), _ptr(out),
+          N, K, group_size, bits, code, _stream(stream))
+    return out
 
 
 def qmv_unpack_codes(w_q, K: int, bits: int, stream=None):

@@ -65,6 +65,67 @@ __global__ __launch_bounds__(256) void pack_kernel(const float *__restrict__ w, 
   }
 }
 
+// ----------------------------------------------------------------------------
+// Dequantize (mlx-metal quantized.h, affine_dequantize): w_hat = s*q + z per
+// group with the stored bf16 scale and bias.  s*q is exact in fp32 (8-bit by
+// 8-bit significands).  The sum with z is split into its fp32 rounding and
+// its exact error (Knuth's TwoSum; the library is built without contraction),
+// so both outputs are the exact value rounded once: fp32 to nearest even, and
+// bf16 to nearest even.
+// ----------------------------------------------------------------------------
+__device__ __forceinline__ uint16_t bf16_of_sum(float hi, float lo) {
+  const uint32_t u = __float_as_uint(hi);
+  // hi is the exact sum rounded to fp32.  Only when hi sits exactly halfway
+  // between two bf16 values can the exact sum round differently from hi, and
+  // then the sign of the error decides (truncating the bits rounds the
+  // magnitude down).
+  if ((u & 0xFFFFu) == 0x8000u && lo != 0.0f) {
+    const bool away = (lo > 0.0f) == (hi > 0.0f);
+    return static_cast<uint16_t>((u >> 16) + (away ? 1u : 0u));
+  }
+  return f32_to_bf16(hi);
+}
+
+template <int BITS>
+__global__ __launch_bounds__(256) void dequant_kernel(const uint32_t *__restrict__ w_q,
+                                                      const uint16_t *__restrict__ scales,
+                                                      const uint16_t *__restrict__ biases,
+                                                      int64_t N, int64_t K, int gshift, int out_f32,
+                                                      void *__restrict__ out) {
+  const int64_t Kc = K >> 5;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (t >= N * Kc) return;
+  const int64_t n = t / Kc, c = t - n * Kc;
+  uint32_t w[BITS];
+  load_chunk<BITS>(w_q + n * Kc * BITS + c * BITS, w);
+  const int64_t gi = n * (Kc >> gshift) + (c >> gshift);
+  const float sf = bf16_to_f32(scales[gi]);
+  const float zf = bf16_to_f32(biases[gi]);
+  float hi[32], lo[32];
+  static_for<0, 32>([&](auto k) {
+    constexpr int Kk = decltype(k)::value;
+    const float p = sf * static_cast<float>(code_at<BITS, Kk>(w));   // exact
+    const float sum = p + zf;
+    const float bb = sum - p;
+    hi[Kk] = sum;
+    lo[Kk] = (p - (sum - bb)) + (zf - bb);
+  });
+  if (out_f32) {
+    float4 *o = reinterpret_cast<float4 *>(static_cast<float *>(out) + n * K + c * 32);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) o[q] = make_float4(hi[4 * q], hi[4 * q + 1], hi[4 * q + 2], hi[4 * q + 3]);
+  } else {
+    uint32_t h[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      h[i] = static_cast<uint32_t>(bf16_of_sum(hi[2 * i], lo[2 * i])) |
+             (static_cast<uint32_t>(bf16_of_sum(hi[2 * i + 1], lo[2 * i + 1])) << 16);
+    uint4 *o = reinterpret_cast<uint4 *>(static_cast<uint16_t *>(out) + n * K + c * 32);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = make_uint4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]);
+  }
+}
+
 // Debug export: unpack with the qmv kernels' own pair / fp32 code builders.
 template <int BITS>
 __global__ __launch_bounds__(256) void unpack_kernel(const uint32_t *__restrict__ w_q, int64_t N,

@@ -205,6 +205,17 @@ int launch_unpack_t(const uint32_t *w_q, int64_t N, int64_t K, uint8_t *codes, h
   return check_launch("qmv_unpack_codes");
 }
 
+template <int BITS>
+int launch_dequant_t(const uint32_t *w_q, const uint16_t *scales, const uint16_t *biases,
+                     int64_t N, int64_t K, int gshift, int out_f32, void *out, hipStream_t st) {
+  const int64_t items = N * (K / 32);
+  const int64_t blocks = (items + 255) / 256;
+  if (blocks > 0x7FFFFFFF) return fail(QMV_EUNSUPPORTED, "qmv_dequantize: too large");
+  hipLaunchKernelGGL(qmvk::dequant_kernel<BITS>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                     st, w_q, scales, biases, N, K, gshift, out_f32, out);
+  return check_launch("qmv_dequantize");
+}
+
 }  // namespace
 
 extern "C" {
@@ -239,6 +250,27 @@ int qmv_unpack_codes(const uint32_t *w_q, int64_t N, int64_t K, int bits, uint8_
     case 5: return launch_unpack_t<5>(w_q, N, K, codes, st);
     case 6: return launch_unpack_t<6>(w_q, N, K, codes, st);
     default: return launch_unpack_t<8>(w_q, N, K, codes, st);
+  }
+}
+
+int qmv_dequantize(const uint32_t *w_q, const uint16_t *scales, const uint16_t *biases, void *out,
+                   int64_t N, int64_t K, int group_size, int bits, int out_dtype, void *stream) {
+  if (int rc = check_common("qmv_dequantize", N, K, group_size, bits)) return rc;
+  if (!w_q || !scales || !biases || !out) return fail(QMV_EINVAL, "qmv_dequantize: null pointer argument");
+  if (out_dtype != QMV_OUT_BF16 && out_dtype != QMV_OUT_F32)
+    return fail(QMV_EINVAL, "qmv_dequantize: out_dtype=%d unknown", out_dtype);
+  if (int rc = check_aligned("qmv_dequantize", w_q, "w_q")) return rc;
+  if (int rc = check_aligned("qmv_dequantize", out, "out")) return rc;
+  const int gs = gshift_of(group_size);
+  const int f32 = out_dtype == QMV_OUT_F32;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  switch (bits) {
+    case 2: return launch_dequant_t<2>(w_q, scales, biases, N, K, gs, f32, out, st);
+    case 3: return launch_dequant_t<3>(w_q, scales, biases, N, K, gs, f32, out, st);
+    case 4: return launch_dequant_t<4>(w_q, scales, biases, N, K, gs, f32, out, st);
+    case 5: return launch_dequant_t<5>(w_q, scales, biases, N, K, gs, f32, out, st);
+    case 6: return launch_dequant_t<6>(w_q, scales, biases, N, K, gs, f32, out, st);
+    default: return launch_dequant_t<8>(w_q, scales, biases, N, K, gs, f32, out, st);
   }
 }
 

@@ -137,6 +137,19 @@ int gather_qmv(const uint16_t *x, int64_t Bx, const uint32_t *w_q,
                int out_dtype, void *stream);
 
 /*
+ * qmv_dequantize -- w_hat[n, k] = scales[n, k/g] * q[n, k] + biases[n, k/g]
+ * (mlx-metal quantized.h, affine_dequantize; mlx.core.dequantize), with the
+ * stored bf16 scale and bias.  out: [N, K], bf16 (QMV_OUT_BF16) or fp32
+ * (QMV_OUT_F32).  Each output is the exact value of s*q + z rounded once to
+ * nearest even, so it equals the oracle's exact result rounded the same way,
+ * bit for bit.  w_q and out must be 16-byte aligned.  Interop and debugging:
+ * not part of the matvec path.
+ */
+int qmv_dequantize(const uint32_t *w_q, const uint16_t *scales,
+                   const uint16_t *biases, void *out, int64_t N, int64_t K,
+                   int group_size, int bits, int out_dtype, void *stream);
+
+/*
  * qmv_unpack_codes -- debugging export: runs the qmv kernels' own in-register
  * unpacking on w_q [N, K*bits/32] and writes one code per byte, codes [N, K].
  */

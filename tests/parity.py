@@ -69,3 +69,29 @@ def check_t2(y_f32, ref, what=""):
     assert err.max() <= tol, (f"{what}: max err {err.max():.3e} > T2 "
                               f"{tol:.3e} at {np.unravel_index(err.argmax(), err.shape)}")
     return float(err.max()), float(err.max() / tol)
+
+
+def bf16_bits_rne_from_f64(v):
+    """Round float64 values once to bf16 bits (nearest, ties to even), from
+    the binary64 fields.  Normal bf16 range and zero only (a value outside
+    raises): what exact dequantized weights need."""
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    u = v.view(np.uint64)
+    sign = (u >> np.uint64(63)).astype(np.uint32)
+    exp = ((u >> np.uint64(52)) & np.uint64(0x7FF)).astype(np.int64)
+    m53 = (u & np.uint64((1 << 52) - 1)) | np.uint64(1 << 52)
+    zero = (u & np.uint64((1 << 63) - 1)) == 0
+    e = exp - 1023
+    if np.any(~zero & ((e < -126) | (e > 127))):
+        raise ValueError("value outside the normal bf16 range")
+    keep = (m53 >> np.uint64(45)).astype(np.int64)           # 8 bits with the leading one
+    rem = m53 & np.uint64((1 << 45) - 1)
+    half = np.uint64(1 << 44)
+    up = (rem > half) | ((rem == half) & ((keep & 1) == 1))
+    keep = keep + up.astype(np.int64)
+    carry = keep == 256
+    keep = np.where(carry, 128, keep)
+    e = e + carry.astype(np.int64)
+    out = (sign << 15) | (((e + 127) & 0xFF).astype(np.uint32) << 7) | (keep & 0x7F).astype(np.uint32)
+    out = np.where(zero, sign << 15, out)
+    return out.astype(np.uint16)

@@ -23,7 +23,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = set(declared_functions())
     assert {"qmv_pack", "qmv", "qmv_gate_up", "qmv_silu_gate_resid",
-            "gather_qmv", "qmv_unpack_codes", "qmv_last_error"} <= names
+            "gather_qmv", "qmv_dequantize", "qmv_unpack_codes",
+            "qmv_last_error"} <= names
 
 
 def test_library_exports_every_declared_symbol():
@@ -103,6 +104,25 @@ def test_unpack_rejects_bad_arguments():
     assert L.qmv_unpack_codes(FAKE, 4, 48, 4, FAKE, None) == q.QMV_EINVAL
     assert L.qmv_unpack_codes(FAKE, 4, 64, 7, FAKE, None) == q.QMV_EINVAL
     assert L.qmv_unpack_codes(None, 4, 64, 4, FAKE, None) == q.QMV_EINVAL
+
+
+def test_dequantize_rejects_bad_arguments():
+    L = q.lib()
+
+    def call(**kw):
+        a = dict(w=FAKE, s=FAKE, b=FAKE, out=FAKE, N=4, K=64, g=64, bits=4, dt=0)
+        a.update(kw)
+        rc = L.qmv_dequantize(a["w"], a["s"], a["b"], a["out"], a["N"], a["K"],
+                              a["g"], a["bits"], a["dt"], None)
+        return rc, L.qmv_last_error().decode()
+    for kw, msg in [(dict(bits=7), "bits=7"), (dict(g=48, K=96), "group_size=48"),
+                    (dict(K=96), "not a multiple"), (dict(N=0), "positive"),
+                    (dict(w=None), "null"), (dict(out=None), "null"),
+                    (dict(dt=2), "out_dtype"),
+                    (dict(out=ctypes.c_void_p(0x1004)), "aligned"),
+                    (dict(w=ctypes.c_void_p(0x1008)), "aligned")]:
+        rc, m = call(**kw)
+        assert rc == q.QMV_EINVAL and msg in m, (kw, rc, m)
 
 
 def test_error_message_clears_on_success_path_is_thread_local():
