@@ -118,6 +118,41 @@ def make_qmv(N, K, bits, g, M, name):
     return Workload(name, nbytes, setup, 1, cpu)
 
 
+def make_qvm(K, N, bits, g, M, name):
+    """transpose = 0: y [M, N] = x [M, K] @ W_hat with W packed [K, N] along
+    N.  Algorithmic bytes: packed W, scales and biases, x and y once (the
+    split-K partial sums are not counted)."""
+    nbytes = qbytes(K, N, bits, g) + 2 * M * K + 2 * M * N
+
+    def setup(dev):
+        import torch
+        import bit_affine_quantized_amd as q
+        import synth
+        w = torch.from_numpy(synth.weight((K, N))).to(dev)
+        w_q, s, b = q.qmv_pack(w, g, bits)
+        del w
+        x = _dev_bf16(torch, synth.activation_bf16((M, K)), dev)
+        sets = max(2, math.ceil(ROTATE_BYTES / nbytes))
+        bufs = [(x.clone(), w_q.clone(), s.clone(), b.clone(),
+                 torch.empty((M, N), dtype=torch.bfloat16, device=dev))
+                for _ in range(sets)]
+
+        def step(i, stream):
+            xb, wb, sb, bb, yb = bufs[i % sets]
+            q.qmv(xb, wb, sb, bb, transpose=False, group_size=g, bits=bits,
+                  y=yb, stream=stream)
+        return step, sets
+
+    def cpu(budget_s):
+        import oracle
+        import synth
+        w_q, s, b = oracle.quantize_pack(synth.weight((K, N)), g, bits)
+        x = synth.activation_bf16((M, K))
+        return lambda: oracle.qvm(x, w_q, s, b, N, g, bits), \
+            f"full {K}x{N} b{bits} g{g} M={M} qvm"
+    return Workload(name, nbytes, setup, 1, cpu)
+
+
 def make_dequant(N, K, bits, g, name):
     """Device dequantize to bf16 [N, K]: reads the packed weight, writes
     2 bytes per weight."""
@@ -303,6 +338,9 @@ def workloads():
         4096, 14336, 8, 64, "ffn_down_silu_resid_4096x14336_b8_g64")
     W["ffn_step_14336x4096_b8_g64"] = make_ffn(
         14336, 4096, 8, 64, "ffn_step_14336x4096_b8_g64")
+    for M in (1, 4):
+        n = f"qvm_4096x4096_b4_g64_m{M}"
+        W[n] = make_qvm(4096, 4096, 4, 64, M, n)
     W["dequant_14336x4096_b4_g64"] = make_dequant(14336, 4096, 4, 64,
                                                   "dequant_14336x4096_b4_g64")
     m = synth.MOE
@@ -346,6 +384,9 @@ def _time_graph(step, steps, warmup):
     runs the launches back to back with no host launch cost in between."""
     import torch
     side = torch.cuda.Stream()
+    with torch.cuda.stream(side):        # per-stream set-up happens outside capture
+        step(0, side)
+    torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=side):
         cs = torch.cuda.current_stream()

@@ -5,11 +5,16 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <map>
+#include <mutex>
 #include <string>
+#include <utility>
+#include <vector>
 
 #include "qmv.h"
 #include "pack_kernels.h"
 #include "qmv_kernels.h"
+#include "qvm_kernels.h"
 
 namespace {
 
@@ -46,18 +51,27 @@ int gshift_of(int g) { return g == 32 ? 0 : g == 64 ? 1 : 2; }
 
 // Shape rules shared by every product (mlx/ops.cpp, extract_quantized_matmul_dims:
 // w is uint32 with K*bits/32 words per row and K/group_size scales per row).
-int check_common(const char *fn, int64_t N, int64_t K, int group_size, int bits) {
+// `packed` is the axis the codes and groups run along (K for the usual
+// x @ W^T; N for transpose = 0), `other` the remaining axis of W.
+int check_shape(const char *fn, int64_t other, const char *other_name, int64_t packed,
+                const char *packed_name, int group_size, int bits) {
   if (!bits_ok(bits)) return fail(QMV_EINVAL, "%s: bits=%d not in {2,3,4,5,6,8}", fn, bits);
   if (!group_ok(group_size))
     return fail(QMV_EINVAL, "%s: group_size=%d not in {32,64,128}", fn, group_size);
-  if (N <= 0 || K <= 0) return fail(QMV_EINVAL, "%s: N=%lld and K=%lld must be positive", fn,
-                                    (long long)N, (long long)K);
-  if (K % group_size != 0)
-    return fail(QMV_EINVAL, "%s: K=%lld is not a multiple of group_size=%d", fn, (long long)K,
-                group_size);
-  if (K > (int64_t(1) << 30) || N > (int64_t(1) << 40))
-    return fail(QMV_EINVAL, "%s: K=%lld or N=%lld too large", fn, (long long)K, (long long)N);
+  if (other <= 0 || packed <= 0)
+    return fail(QMV_EINVAL, "%s: %s=%lld and %s=%lld must be positive", fn, other_name,
+                (long long)other, packed_name, (long long)packed);
+  if (packed % group_size != 0)
+    return fail(QMV_EINVAL, "%s: %s=%lld is not a multiple of group_size=%d", fn, packed_name,
+                (long long)packed, group_size);
+  if (packed > (int64_t(1) << 30) || other > (int64_t(1) << 40))
+    return fail(QMV_EINVAL, "%s: %s=%lld or %s=%lld too large", fn, packed_name, (long long)packed,
+                other_name, (long long)other);
   return QMV_OK;
+}
+
+int check_common(const char *fn, int64_t N, int64_t K, int group_size, int bits) {
+  return check_shape(fn, N, "N", K, "K", group_size, bits);
 }
 
 // The kernels read x (and gate/up) and packed rows with 16-byte vector loads.
@@ -205,6 +219,118 @@ int launch_unpack_t(const uint32_t *w_q, int64_t N, int64_t K, uint8_t *codes, h
   return check_launch("qmv_unpack_codes");
 }
 
+// ------------------------------------------------------------------ qvm
+// Workspace of the split-K qvm (its partial sums): per (device, stream),
+// grown on demand and held until the process ends.  A buffer that is
+// outgrown is kept, not freed, so a HIP graph captured with it stays valid.
+struct Workspace {
+  void *ptr = nullptr;
+  size_t bytes = 0;
+};
+std::mutex g_ws_mu;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+std::vector<void *> g_ws_retired;
+
+int workspace_for(hipStream_t st, size_t bytes, void **out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(QMV_EHIP, "qmv: hipGetDevice failed");
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  Workspace &w = g_ws[{dev, st}];
+  if (w.bytes < bytes) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone)
+      return fail(QMV_EUNSUPPORTED,
+                  "qmv: transpose=0 needs a %zu-byte workspace on this stream; make one call of "
+                  "this size (or larger) on the stream before capturing it", bytes);
+    void *p = nullptr;
+    if (hipMalloc(&p, bytes) != hipSuccess)
+      return fail(QMV_EHIP, "qmv: workspace allocation of %zu bytes failed", bytes);
+    if (w.ptr) g_ws_retired.push_back(w.ptr);
+    w.ptr = p;
+    w.bytes = bytes;
+  }
+  *out = w.ptr;
+  return QMV_OK;
+}
+
+constexpr int kQvmRows = 4;   // rows in flight per stream
+
+template <int BITS, int MV>
+int launch_qvm_t(const qmvk::QvmArgs &a0, hipStream_t st) {
+  qmvk::QvmArgs a = a0;
+  const int64_t Nc = a.N / 32;
+  const int64_t CB = (Nc + qmvk::kQvmC - 1) / qmvk::kQvmC;
+  const int64_t unit = static_cast<int64_t>(kQvmRows) * qmvk::kQvmStreams;
+  // ~1024 workgroups, at most 64 slices, whole blocks of rows per slice
+  int64_t s_target = 1024 / CB;
+  if (s_target < 1) s_target = 1;
+  if (s_target > 64) s_target = 64;
+  int64_t ks = (a.K + s_target - 1) / s_target;
+  ks = ((ks + unit - 1) / unit) * unit;
+  if (ks > 1024) ks = 1024;             // the staged x slice stays small beside the sums
+  const int64_t S = (a.K + ks - 1) / ks;
+  if (CB * S > 0x7FFFFFFF) return fail(QMV_EUNSUPPORTED, "qmv: transpose=0 grid too large");
+  const int64_t lds = 4 * (MV * ks + static_cast<int64_t>(qmvk::kQvmStreams) * MV * (qmvk::kQvmCols * 9 / 8));
+  if (lds > kMaxLds) return fail(QMV_EUNSUPPORTED, "qmv: transpose=0 with K=%d too large", a.K);
+  a.S = static_cast<int>(S);
+  a.ks = static_cast<int>(ks);
+  if (S > 1) {
+    void *ws = nullptr;
+    if (int rc = workspace_for(st, static_cast<size_t>(S) * MV * a.N * 4, &ws)) return rc;
+    a.part = static_cast<float *>(ws);
+  }
+  auto kern = qmvk::qvm_kernel<BITS, MV, kQvmRows>;
+  allow_lds(kern, lds);
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(CB * S)), dim3(qmvk::kQvmWaves * qmvk::kWave),
+                     static_cast<size_t>(lds), st, a);
+  if (int rc = check_launch("qmv (transpose=0)")) return rc;
+  if (S > 1) {
+    const int64_t outs = static_cast<int64_t>(a.M) * a.N;
+    hipLaunchKernelGGL(qmvk::qvm_reduce_kernel, dim3(static_cast<unsigned>((outs + 255) / 256)),
+                       dim3(256), 0, st, a.part, a.S, MV, a.M, a.N, a.y_ld, a.out_f32, a.y);
+    return check_launch("qmv (transpose=0) reduce");
+  }
+  return QMV_OK;
+}
+
+template <int MV>
+int launch_qvm_bits(int bits, const qmvk::QvmArgs &a, hipStream_t st) {
+  switch (bits) {
+    case 2: return launch_qvm_t<2, MV>(a, st);
+    case 3: return launch_qvm_t<3, MV>(a, st);
+    case 4: return launch_qvm_t<4, MV>(a, st);
+    case 5: return launch_qvm_t<5, MV>(a, st);
+    case 6: return launch_qvm_t<6, MV>(a, st);
+    case 8: return launch_qvm_t<8, MV>(a, st);
+  }
+  return fail(QMV_EINVAL, "bits=%d", bits);
+}
+
+// y = x @ W_hat with W packed [K, N] along N: slabs of up to 2 vectors.
+int run_qvm(const uint16_t *x, const uint32_t *w_q, const uint16_t *scales, const uint16_t *biases,
+            void *y, int64_t M, int64_t N, int64_t K, int group_size, int bits, int out_f32,
+            hipStream_t st) {
+  for (int64_t m0 = 0; m0 < M; m0 += 2) {
+    qmvk::QvmArgs a{};
+    const int64_t nv = M - m0 < 2 ? M - m0 : 2;
+    a.x = x + m0 * K;
+    a.w = w_q;
+    a.s = scales;
+    a.b = biases;
+    a.y = out_f32 ? static_cast<void *>(static_cast<float *>(y) + m0 * N)
+                  : static_cast<void *>(static_cast<uint16_t *>(y) + m0 * N);
+    a.N = N;
+    a.y_ld = N;
+    a.K = static_cast<int>(K);
+    a.M = static_cast<int>(nv);
+    a.gshift = gshift_of(group_size);
+    a.out_f32 = out_f32;
+    const int rc = nv == 1 ? launch_qvm_bits<1>(bits, a, st) : launch_qvm_bits<2>(bits, a, st);
+    if (rc) return rc;
+  }
+  return ok();
+}
+
 template <int BITS>
 int launch_dequant_t(const uint32_t *w_q, const uint16_t *scales, const uint16_t *biases,
                      int64_t N, int64_t K, int gshift, int out_f32, void *out, hipStream_t st) {
@@ -277,13 +403,22 @@ int qmv_dequantize(const uint32_t *w_q, const uint16_t *scales, const uint16_t *
 int qmv(const uint16_t *x, const uint32_t *w_q, const uint16_t *scales, const uint16_t *biases,
         void *y, int64_t M, int64_t N, int64_t K, int group_size, int bits, int transpose,
         int out_dtype, void *stream) {
-  if (int rc = check_common("qmv", N, K, group_size, bits)) return rc;
+  if (transpose != 0 && transpose != 1)
+    return fail(QMV_EINVAL, "qmv: transpose=%d must be 0 or 1", transpose);
+  // the packed (group) axis is K for transpose = 1 and N for transpose = 0
+  if (int rc = transpose ? check_common("qmv", N, K, group_size, bits)
+                         : check_shape("qmv (transpose=0)", K, "K", N, "N", group_size, bits)) return rc;
   if (M <= 0) return fail(QMV_EINVAL, "qmv: M=%lld must be positive", (long long)M);
   if (!x || !w_q || !scales || !biases || !y) return fail(QMV_EINVAL, "qmv: null pointer argument");
   if (out_dtype != QMV_OUT_BF16 && out_dtype != QMV_OUT_F32)
     return fail(QMV_EINVAL, "qmv: out_dtype=%d unknown", out_dtype);
-  if (transpose != 1)
-    return fail(QMV_EUNSUPPORTED, "qmv: transpose=0 (x @ W with W packed [K,N]) is not implemented");
+  if (transpose == 0) {
+    if (int rc = check_aligned("qmv", w_q, "w_q")) return rc;
+    if (K > (int64_t(1) << 30) || M > (int64_t(1) << 30))
+      return fail(QMV_EUNSUPPORTED, "qmv: transpose=0 with K or M too large");
+    return run_qvm(x, w_q, scales, biases, y, M, N, K, group_size, bits, out_dtype == QMV_OUT_F32,
+                   static_cast<hipStream_t>(stream));
+  }
   if (int rc = check_aligned("qmv", x, "x")) return rc;
   if (int rc = check_aligned("qmv", w_q, "w_q")) return rc;
   const int mv_max = qmv_lds_bytes(bits, 4, K) <= kMaxLds ? 4

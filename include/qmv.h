@@ -78,10 +78,21 @@ int qmv_pack(const float *w, int64_t N, int64_t K, int group_size, int bits,
  * qmv -- quantized matmul at decode batch sizes (mlx/ops.cpp quantized_matmul;
  * quantized.h qmv_fast / qmv kernels).
  *   transpose = 1: W packed [N, K]; y[m, n] = sum_k x[m, k] * w_hat[n, k].
- *   transpose = 0: W packed [K, N] (groups along N); y = x @ w_hat.
- *                  Not implemented in this build: returns QMV_EUNSUPPORTED.
- * x: bf16 [M, K].  y: [M, N], bf16 or fp32 per out_dtype.  M >= 1 (the W
- * stream is read once per slab of up to 4 rows of x).
+ *                  K must be a multiple of group_size.  The W stream is read
+ *                  once per slab of up to 4 rows of x.
+ *   transpose = 0: W packed [K, N] (groups along N, quantized.h qvm and its
+ *                  split-K variant); y[m, n] = sum_k x[m, k] * w_hat[k, n].
+ *                  N must be a multiple of group_size; W is read once per
+ *                  slab of up to 2 rows of x.  K is split into slices whose
+ *                  partial sums go to a library-held workspace (per device
+ *                  and stream, allocated on first use, kept until the
+ *                  process ends) and are added in a fixed order, so results
+ *                  are reproducible.  Under HIP graph capture a call that
+ *                  would need a new or larger workspace returns
+ *                  QMV_EUNSUPPORTED: make one eager call of that size on the
+ *                  stream first.  Calls on one stream share its workspace
+ *                  (stream order serializes them).
+ * x: bf16 [M, K].  y: [M, N], bf16 or fp32 per out_dtype.  M >= 1.
  */
 int qmv(const uint16_t *x, const uint32_t *w_q, const uint16_t *scales,
         const uint16_t *biases, void *y, int64_t M, int64_t N, int64_t K,

@@ -56,7 +56,11 @@ def _qmv(**kw):
     (dict(w=None), q.QMV_EINVAL, "null"),
     (dict(y=None), q.QMV_EINVAL, "null"),
     (dict(out=2), q.QMV_EINVAL, "out_dtype"),
-    (dict(transpose=0), q.QMV_EUNSUPPORTED, "transpose=0"),
+    (dict(transpose=2), q.QMV_EINVAL, "transpose=2"),
+    # transpose=0 packs along N: N must be a multiple of the group size
+    (dict(transpose=0, N=48, K=64), q.QMV_EINVAL, "N=48 is not a multiple"),
+    (dict(transpose=0, N=64, K=0), q.QMV_EINVAL, "positive"),
+    (dict(transpose=0, N=128, w=ctypes.c_void_p(0x1008)), q.QMV_EINVAL, "aligned"),
     (dict(x=ctypes.c_void_p(0x1002)), q.QMV_EINVAL, "aligned"),
     (dict(w=ctypes.c_void_p(0x1008)), q.QMV_EINVAL, "aligned"),
 ])

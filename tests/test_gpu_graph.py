@@ -68,3 +68,33 @@ def test_ffn_graph_replays_match_eager(dev):
         torch.cuda.synchronize()
         np.testing.assert_array_equal(bf16_to_np_bits(y), y_eager,
                                       err_msg=f"replay {rep}")
+
+
+def test_qvm_graph_replays_match_eager(dev):
+    """transpose = 0 under capture: a warm-up call first sets up the stream's
+    split-K workspace, then every replay must reproduce the eager bits."""
+    import torch
+
+    import bit_affine_quantized_amd as q
+    K, N, g, bits = 4096, 2048, 64, 4
+    w_q, s, b = oracle.quantize_pack(synth.weight((K, N), 0), g, bits)
+    w = (to_dev_u32(w_q, dev), to_dev_bf16(s, dev), to_dev_bf16(b, dev))
+    x = to_dev_bf16(synth.activation_bf16((1, K), 5), dev)
+    side = torch.cuda.Stream()
+    y = torch.zeros((1, N), dtype=torch.bfloat16, device=dev)
+    with torch.cuda.stream(side):
+        q.qmv(x, *w, transpose=False, group_size=g, bits=bits, y=y)   # warm-up
+    torch.cuda.synchronize()
+    y_eager = bf16_to_np_bits(y)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        q.qmv(x, *w, transpose=False, group_size=g, bits=bits, y=y)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        y.zero_()
+        junk = q.qmv(x, *w, transpose=False, group_size=g, bits=bits)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(bf16_to_np_bits(y), y_eager, err_msg=f"replay {rep}")
+        del junk
