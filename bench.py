@@ -338,6 +338,9 @@ def workloads():
         4096, 14336, 8, 64, "ffn_down_silu_resid_4096x14336_b8_g64")
     W["ffn_step_14336x4096_b8_g64"] = make_ffn(
         14336, 4096, 8, 64, "ffn_step_14336x4096_b8_g64")
+    for M in (8, 16, 64):
+        n = f"qmm_4096x4096_b4_g64_m{M}"
+        W[n] = make_qmv(4096, 4096, 4, 64, M, n)
     for M in (1, 4):
         n = f"qvm_4096x4096_b4_g64_m{M}"
         W[n] = make_qvm(4096, 4096, 4, 64, M, n)

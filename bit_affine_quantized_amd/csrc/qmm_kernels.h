@@ -1,0 +1,282 @@
+// qmm: the transposed quantized product for several x rows at once (prefill
+// and batched decode; mlx-metal quantized.h qmm_t), y[m, n] =
+// sum_k x[m, k] * w_hat[n, k], on the matrix cores.
+//
+// The magic-bf16 codes of the matvec path carry over exactly: a b-bit code q
+// placed in the top of a bf16 mantissa with exponent 2^7 is the bf16 value
+// 128 + q * 2^P (P = 7 - b), so one v_mfma_f32_16x16x32_bf16 on a 32-code
+// chunk gives D = 128 * X + 2^P * sum q x for 16 W rows by 16 x rows, X being
+// the chunk's sum of x.  Chaining the chunks of a group and folding once per
+// group, y = 2^-P s D + (z - 2^b s) X, with exact operands: products of bf16
+// values are exact and the accumulation is fp32.  8-bit codes do not fit the
+// 7-bit mantissa and are split into nibbles, q = lo + 16 hi, with one MFMA
+// each: y = (s / 8)(D_lo + 16 D_hi) + (z - 272 s) X.
+//
+// The contraction order inside one MFMA is free, so the 32 k of a chunk are
+// taken in the pairing order (8i + j, 8i + j + 4) for every bit width: lane
+// group i (= lane / 16) of the B operand holds codes 8i..8i+7, read from a
+// byte-aligned window of the chunk, and x is staged once per workgroup in the
+// same order.
+//
+// A workgroup (4 waves) covers 64 W rows (16 per wave) by up to 64 x rows
+// (BM m-tiles) over a slice of K; x is staged in LDS 8 chunks at a time.  A
+// slice's fp32 result goes to y directly, or, with several slices, to the
+// workspace, whose slices are then added in order by a second kernel.
+#pragma once
+
+#include "qmv_device.h"
+
+namespace qmvk {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+struct QmmArgs {
+  const uint16_t *x;        // [M, K] bf16 (this launch's rows)
+  const uint32_t *w;        // [N, K*bits/32]
+  const uint16_t *s, *b;    // [N, K/g]
+  float *part;              // [S, 16*BM, N] (S > 1)
+  void *y;                  // [M, N] (row stride y_ld)
+  int64_t N;
+  int64_t y_ld;
+  int K;
+  int M;                    // x rows in this launch (<= 16*BM)
+  int gshift;               // log2(group_size / 32)
+  int S;                    // K-slices
+  int cps;                  // chunks per slice (a multiple of kQmmKB)
+  int out_f32;
+};
+
+constexpr int kQmmKB = 8;          // chunks per staged K-block
+constexpr int kQmmRow = 80;        // bytes per staged (x row, chunk): 64 B of pairs + pad
+constexpr int kQmmRowsPerWG = 64;  // W rows per workgroup
+
+template <int BM>
+constexpr int qmm_lds_bytes() {
+  return kQmmKB * 16 * BM * kQmmRow + kQmmKB * 16 * BM * 4;
+}
+
+// The 8 codes 8i..8i+7 of a chunk (lane group i), as a 64-bit window whose
+// bits [0, 8b) hold them in order.  b <= 6: the window is byte-aligned at
+// byte b*i of the chunk; a second word is read only when the codes cross a
+// word (otherwise the first word is read again: no read past the chunk).
+template <int BITS>
+__device__ __forceinline__ void qmm_load_window(const uint32_t *__restrict__ chunk, int i,
+                                                uint32_t &w0, uint32_t &w1, uint32_t &shift) {
+  if constexpr (BITS == 8) {
+    const u32x2_t v = stream_load(reinterpret_cast<const u32x2_t *>(chunk) + i);
+    w0 = v.x;
+    w1 = v.y;
+    shift = 0;
+  } else {
+    const int byte0 = BITS * i;
+    const int wd = byte0 >> 2;
+    const int second = ((byte0 & 3) + BITS > 4) ? 1 : 0;
+    w0 = stream_load(chunk + wd);
+    w1 = stream_load(chunk + wd + second);
+    shift = static_cast<uint32_t>(byte0 & 3) * 8u;
+  }
+}
+
+// Magic-bf16 B operand (4 dwords = 8 bf16) from the lane's window: pair j
+// holds codes j (low half) and j + 4 (high half).
+template <int BITS>
+__device__ __forceinline__ void qmm_b_pairs(uint32_t w0, uint32_t w1, uint32_t shift,
+                                            const PairConsts &pk, uint32_t (&p)[4]) {
+  if constexpr (BITS == 4) {
+    // codes j, j+4 are nibbles j, j+4 of one word: the matvec's 4-bit plan
+    const uint32_t w[4] = {w0, w0, w0, w0};
+    static_for<0, 4>([&](auto jj) {
+      constexpr int J = decltype(jj)::value;
+      p[J] = make_pair<4, J>(w, pk);
+    });
+  } else if constexpr (BITS == 2) {
+    // 8 codes = 16 bits; spread codes 4..7 to the high half, then the
+    // matvec's 2-bit plan (pair j = codes at bits 2j and 2j + 16)
+    const uint32_t v = (w0 >> shift) & 0xFFFFu;
+    const uint32_t t = (v & 0xFFu) | ((v & 0xFF00u) << 8);
+    const uint32_t w[2] = {t, t};
+    static_for<0, 4>([&](auto jj) {
+      constexpr int J = decltype(jj)::value;
+      p[J] = make_pair<2, J>(w, pk);
+    });
+  } else {
+    constexpr int P = 7 - BITS;
+    constexpr uint32_t mask = (1u << BITS) - 1u;
+    const uint64_t v = ((static_cast<uint64_t>(w1) << 32) | w0) >> shift;
+    static_for<0, 4>([&](auto jj) {
+      constexpr int J = decltype(jj)::value;
+      const uint32_t lo = static_cast<uint32_t>(v >> (BITS * J)) & mask;
+      const uint32_t hi = static_cast<uint32_t>(v >> (BITS * (J + 4))) & mask;
+      p[J] = (lo << P) | (hi << (16 + P)) | pk.magic;
+    });
+  }
+}
+
+// 8-bit codes: nibble operands.  Pair j takes bytes j (of w0) and j (of w1),
+// i.e. codes j and j + 4; `lo` holds their low nibbles, `hi` their high ones.
+__device__ __forceinline__ void qmm_b_nibbles(uint32_t w0, uint32_t w1, const PairConsts &pk,
+                                              uint32_t (&lo)[4], uint32_t (&hi)[4]) {
+  static_for<0, 4>([&](auto jj) {
+    constexpr int J = decltype(jj)::value;
+    // bytes: out0 = w0.byte J, out2 = w1.byte J, out1 = out3 = 0
+    constexpr uint32_t sel = (0x0Cu << 24) | ((4u + J) << 16) | (0x0Cu << 8) | J;
+    const uint32_t t = __builtin_amdgcn_perm(w1, w0, sel);
+    lo[J] = ((t << 3) & pk.mask) | pk.magic;
+    hi[J] = ((t >> 1) & pk.mask) | pk.magic;
+  });
+}
+
+template <int BITS, int BM, int CPG>
+__global__ __launch_bounds__(256) void qmm_kernel(QmmArgs a) {
+  constexpr int MR = 16 * BM;                     // x rows per launch
+  constexpr bool NIB = BITS == 8;
+  constexpr int P = NIB ? 3 : 7 - BITS;
+  constexpr float kZc = NIB ? 272.0f : static_cast<float>(1 << BITS);   // z - kZc * s
+  constexpr int GPB = kQmmKB / CPG;               // groups per K-block
+  extern __shared__ __align__(16) unsigned char smem[];
+  unsigned char *xp = smem;                                       // [KB][MR][80]
+  float *xsum = reinterpret_cast<float *>(smem + kQmmKB * MR * kQmmRow);   // [KB][MR]
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int j = lane & 15, kb = lane >> 4;
+  const int64_t NB = (a.N + kQmmRowsPerWG - 1) / kQmmRowsPerWG;
+  const int64_t nb = blockIdx.x % NB;
+  const int sl = static_cast<int>(blockIdx.x / NB);
+  const int64_t n = nb * kQmmRowsPerWG + wid * 16 + j;
+  const uint32_t nrow = static_cast<uint32_t>(n < a.N ? n : a.N - 1);   // rows past N: not stored
+  const int Kc = a.K >> 5;
+  const int c0 = sl * a.cps;
+  const int c1 = min(Kc, c0 + a.cps);
+  const uint32_t gpr = static_cast<uint32_t>(Kc / CPG);           // groups per row
+  // 32-bit byte offsets from the arrays' scalar bases (the host keeps every
+  // array under 4 GiB for this path)
+  const uint32_t wlane = nrow * static_cast<uint32_t>(Kc * BITS * 4) +
+                         (NIB ? static_cast<uint32_t>(kb) * 8u : static_cast<uint32_t>(BITS * kb) & ~3u);
+  const uint32_t w_second = NIB ? 4u : ((((BITS * kb) & 3) + BITS > 4) ? 4u : 0u);
+  const uint32_t w_shift = NIB ? 0u : static_cast<uint32_t>((BITS * kb) & 3) * 8u;
+  const PairConsts pk = pair_consts<NIB ? 4 : (BITS <= 6 ? BITS : 4)>();
+
+  f32x4_t acc[BM], accz[BM], D[BM], Dh[BM];
+#pragma unroll
+  for (int t = 0; t < BM; ++t) {
+    acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    accz[t] = acc[t];
+    D[t] = acc[t];
+    Dh[t] = acc[t];
+  }
+
+  for (int cb = c0; cb < c1; cb += kQmmKB) {
+    // this block's weight windows, scales and biases first: their latency
+    // overlaps the staging (chunks past the slice re-read its last chunk)
+    uint32_t w0[kQmmKB], w1[kQmmKB];
+    uint16_t sv[GPB], zv[GPB];
+#pragma unroll
+    for (int cc = 0; cc < kQmmKB; ++cc) {
+      const uint32_t c = static_cast<uint32_t>(min(cb + cc, c1 - 1));
+      const uint32_t off = wlane + c * (BITS * 4);
+      w0[cc] = stream_load(byte_offset(a.w, off));
+      w1[cc] = stream_load(byte_offset(a.w, off + w_second));
+    }
+#pragma unroll
+    for (int gg = 0; gg < GPB; ++gg) {
+      const uint32_t gi = static_cast<uint32_t>(min(cb + gg * CPG, c1 - 1)) / CPG;
+      sv[gg] = *byte_offset(a.s, (nrow * gpr + gi) * 2u);
+      zv[gg] = *byte_offset(a.b, (nrow * gpr + gi) * 2u);
+    }
+    __syncthreads();                              // the previous block's LDS reads are done
+    // ---- stage x rows [0, MR) x chunks [cb, cb + KB) in pair order.  Rows
+    // past M and chunks past the slice restage a valid row / chunk: their
+    // products only reach outputs that are never stored or never consumed.
+    for (int it = threadIdx.x; it < MR * kQmmKB; it += 256) {
+      const int r = it / kQmmKB, cc = it - r * kQmmKB;
+      const int rr = min(r, a.M - 1), c = min(cb + cc, c1 - 1);
+      uint32_t raw[16];
+      load_x_chunk(byte_offset(a.x, static_cast<uint32_t>(rr * a.K + c * 32) * 2u), raw);
+      float sum = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) sum = dot2_bf16(raw[q], 0x3F803F80u, sum);
+      unsigned char *dst = xp + (cc * MR + r) * kQmmRow;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t pr[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // pair 4q + e = (x[8q + e], x[8q + e + 4])
+          pr[e] = __builtin_amdgcn_perm(raw[4 * q + 2 + (e >> 1)], raw[4 * q + (e >> 1)],
+                                        (e & 1) ? 0x07060302u : 0x05040100u);
+        }
+        *reinterpret_cast<uint4 *>(dst + q * 16) = make_uint4(pr[0], pr[1], pr[2], pr[3]);
+      }
+      xsum[cc * MR + r] = sum;
+    }
+    __syncthreads();
+
+    static_for<0, kQmmKB>([&](auto ccv) {
+      constexpr int cc = decltype(ccv)::value;
+      constexpr bool first = cc % CPG == 0, last = cc % CPG == CPG - 1;
+      if (cb + cc < c1) {                         // uniform; groups are whole
+        uint32_t bp[4], bh[4];
+        if constexpr (NIB) qmm_b_nibbles(w0[cc], w1[cc], pk, bp, bh);
+        else qmm_b_pairs<BITS>(w0[cc], w1[cc], w_shift, pk, bp);
+        const bf16x8_t B = __builtin_bit_cast(bf16x8_t, make_uint4(bp[0], bp[1], bp[2], bp[3]));
+        const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < BM; ++t) {
+          const uint4 av = *reinterpret_cast<const uint4 *>(xp + (cc * MR + t * 16 + j) * kQmmRow + kb * 16);
+          const bf16x8_t A = __builtin_bit_cast(bf16x8_t, av);
+          D[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, first ? zero : D[t], 0, 0, 0);
+          if constexpr (NIB) {
+            const bf16x8_t Bh = __builtin_bit_cast(bf16x8_t, make_uint4(bh[0], bh[1], bh[2], bh[3]));
+            Dh[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bh, first ? zero : Dh[t], 0, 0, 0);
+          }
+        }
+        if constexpr (last) {                     // fold the group
+          const float s = bf16_to_f32(sv[cc / CPG]);
+          const float zc = fmaf(-kZc, s, bf16_to_f32(zv[cc / CPG]));
+#pragma unroll
+          for (int t = 0; t < BM; ++t) {
+            float4 xg = *reinterpret_cast<const float4 *>(xsum + (cc - CPG + 1) * MR + t * 16 + 4 * kb);
+#pragma unroll
+            for (int q = 1; q < CPG; ++q) {
+              const float4 v = *reinterpret_cast<const float4 *>(xsum + (cc - CPG + 1 + q) * MR + t * 16 + 4 * kb);
+              xg.x += v.x; xg.y += v.y; xg.z += v.z; xg.w += v.w;
+            }
+            const float xgv[4] = {xg.x, xg.y, xg.z, xg.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float d = NIB ? fmaf(16.0f, Dh[t][e], D[t][e]) : D[t][e];
+              acc[t][e] = fmaf(s, d, acc[t][e]);
+              accz[t][e] = fmaf(zc, xgv[e], accz[t][e]);
+            }
+          }
+        }
+      }
+    });
+  }
+
+  // ---- lane holds rows 4*kb + e of each m-tile, column n
+  constexpr float kInvP = 1.0f / static_cast<float>(1 << P);
+#pragma unroll
+  for (int t = 0; t < BM; ++t) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int m = t * 16 + 4 * kb + e;
+      const float v = fmaf(acc[t][e], kInvP, accz[t][e]);
+      if (n < a.N) {
+        if (a.S == 1) {
+          if (m < a.M) {
+            const int64_t o = static_cast<int64_t>(m) * a.y_ld + n;
+            if (a.out_f32) static_cast<float *>(a.y)[o] = v;
+            else static_cast<uint16_t *>(a.y)[o] = f32_to_bf16(v);
+          }
+        } else {
+          a.part[(static_cast<int64_t>(sl) * MR + m) * a.N + n] = v;
+        }
+      }
+    }
+  }
+}
+
+}  // namespace qmvk

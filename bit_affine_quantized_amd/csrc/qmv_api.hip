@@ -15,6 +15,7 @@
 #include "pack_kernels.h"
 #include "qmv_kernels.h"
 #include "qvm_kernels.h"
+#include "qmm_kernels.h"
 
 namespace {
 
@@ -331,6 +332,103 @@ int run_qvm(const uint16_t *x, const uint32_t *w_q, const uint16_t *scales, cons
   return ok();
 }
 
+// ------------------------------------------------------------------ qmm
+#ifndef QMV_QMM_MIN_M
+// x rows from which transpose=1 uses the matrix cores (4096x4096 4-bit on
+// MI355X: M = 8 slabs 11.7 us vs MFMA 16.9 us; M = 16 22.6 us vs 17.1 us)
+#define QMV_QMM_MIN_M 12
+#endif
+#ifndef QMV_QMM_WGS
+#define QMV_QMM_WGS 512           // split-K target: workgroups per launch
+#endif
+
+template <int BITS, int BM, int CPG>
+int launch_qmm_t(const qmvk::QmmArgs &a0, hipStream_t st) {
+  qmvk::QmmArgs a = a0;
+  constexpr int MR = 16 * BM;
+  const int64_t Kc = a.K / 32;
+  const int64_t NB = (a.N + qmvk::kQmmRowsPerWG - 1) / qmvk::kQmmRowsPerWG;
+  const int64_t blocks = (Kc + qmvk::kQmmKB - 1) / qmvk::kQmmKB;
+  int64_t S = (QMV_QMM_WGS + NB - 1) / NB;
+  if (S > blocks) S = blocks;
+  if (S < 1) S = 1;
+  const int64_t cps = ((blocks + S - 1) / S) * qmvk::kQmmKB;   // chunks per slice
+  S = (Kc + cps - 1) / cps;
+  if (NB * S > 0x7FFFFFFF) return fail(QMV_EUNSUPPORTED, "qmv: grid too large");
+  a.S = static_cast<int>(S);
+  a.cps = static_cast<int>(cps);
+  if (S > 1) {
+    void *ws = nullptr;
+    if (int rc = workspace_for(st, static_cast<size_t>(S) * MR * a.N * 4, &ws)) return rc;
+    a.part = static_cast<float *>(ws);
+  }
+  constexpr int lds = qmvk::qmm_lds_bytes<BM>();
+  auto kern = qmvk::qmm_kernel<BITS, BM, CPG>;
+  allow_lds(kern, lds);
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(NB * S)), dim3(256), lds, st, a);
+  if (int rc = check_launch("qmv (matrix cores)")) return rc;
+  if (S > 1) {
+    const int64_t outs = static_cast<int64_t>(a.M) * a.N;
+    hipLaunchKernelGGL(qmvk::qvm_reduce_kernel, dim3(static_cast<unsigned>((outs + 255) / 256)),
+                       dim3(256), 0, st, a.part, a.S, MR, a.M, a.N, a.y_ld, a.out_f32, a.y);
+    return check_launch("qmv (matrix cores) reduce");
+  }
+  return QMV_OK;
+}
+
+template <int BITS, int CPG>
+int launch_qmm_bm(int bm, const qmvk::QmmArgs &a, hipStream_t st) {
+  switch (bm) {
+    case 1: return launch_qmm_t<BITS, 1, CPG>(a, st);
+    case 2: return launch_qmm_t<BITS, 2, CPG>(a, st);
+    case 3: return launch_qmm_t<BITS, 3, CPG>(a, st);
+    default: return launch_qmm_t<BITS, 4, CPG>(a, st);
+  }
+}
+
+template <int BITS>
+int launch_qmm_g(int bm, const qmvk::QmmArgs &a, hipStream_t st) {
+  switch (a.gshift) {
+    case 0: return launch_qmm_bm<BITS, 1>(bm, a, st);
+    case 1: return launch_qmm_bm<BITS, 2>(bm, a, st);
+    default: return launch_qmm_bm<BITS, 4>(bm, a, st);
+  }
+}
+
+// y = x @ W_hat^T for many rows of x: slabs of up to 64 rows on the matrix cores.
+int run_qmm(const uint16_t *x, const uint32_t *w_q, const uint16_t *scales, const uint16_t *biases,
+            void *y, int64_t M, int64_t N, int64_t K, int group_size, int bits, int out_f32,
+            hipStream_t st) {
+  for (int64_t m0 = 0; m0 < M; m0 += 64) {
+    const int64_t rows = M - m0 < 64 ? M - m0 : 64;
+    qmvk::QmmArgs a{};
+    a.x = x + m0 * K;
+    a.w = w_q;
+    a.s = scales;
+    a.b = biases;
+    a.y = out_f32 ? static_cast<void *>(static_cast<float *>(y) + m0 * N)
+                  : static_cast<void *>(static_cast<uint16_t *>(y) + m0 * N);
+    a.N = N;
+    a.y_ld = N;
+    a.K = static_cast<int>(K);
+    a.M = static_cast<int>(rows);
+    a.gshift = gshift_of(group_size);
+    a.out_f32 = out_f32;
+    const int bm = static_cast<int>((rows + 15) / 16);
+    int rc;
+    switch (bits) {
+      case 2: rc = launch_qmm_g<2>(bm, a, st); break;
+      case 3: rc = launch_qmm_g<3>(bm, a, st); break;
+      case 4: rc = launch_qmm_g<4>(bm, a, st); break;
+      case 5: rc = launch_qmm_g<5>(bm, a, st); break;
+      case 6: rc = launch_qmm_g<6>(bm, a, st); break;
+      default: rc = launch_qmm_g<8>(bm, a, st); break;
+    }
+    if (rc) return rc;
+  }
+  return ok();
+}
+
 template <int BITS>
 int launch_dequant_t(const uint32_t *w_q, const uint16_t *scales, const uint16_t *biases,
                      int64_t N, int64_t K, int gshift, int out_f32, void *out, hipStream_t st) {
@@ -421,6 +519,14 @@ int qmv(const uint16_t *x, const uint32_t *w_q, const uint16_t *scales, const ui
   }
   if (int rc = check_aligned("qmv", x, "x")) return rc;
   if (int rc = check_aligned("qmv", w_q, "w_q")) return rc;
+  if (M >= QMV_QMM_MIN_M && N * K * bits / 8 < (int64_t(1) << 32) &&
+      N * (K / group_size) * 2 < (int64_t(1) << 32) && 64 * K * 2 < (int64_t(1) << 32)) {
+    // (the matrix-core kernel addresses W, scales and biases and a 64-row
+    // slab of x with 32-bit byte offsets)
+    if (M > (int64_t(1) << 30)) return fail(QMV_EUNSUPPORTED, "qmv: M=%lld too large", (long long)M);
+    return run_qmm(x, w_q, scales, biases, y, M, N, K, group_size, bits, out_dtype == QMV_OUT_F32,
+                   static_cast<hipStream_t>(stream));
+  }
   const int mv_max = qmv_lds_bytes(bits, 4, K) <= kMaxLds ? 4
                    : qmv_lds_bytes(bits, 2, K) <= kMaxLds ? 2
                    : qmv_lds_bytes(bits, 1, K) <= kMaxLds ? 1 : 0;
