@@ -127,28 +127,25 @@ __device__ __forceinline__ void qmm_b_nibbles(uint32_t w0, uint32_t w1, const Pa
   });
 }
 
-template <int BITS, int BM, int CPG>
-__global__ __launch_bounds__(256) void qmm_kernel(QmmArgs a) {
-  constexpr int MR = 16 * BM;                     // x rows per launch
+// One workgroup's contribution over chunks [c0, c1) of W rows nb*64 .. +64
+// (wave wid: 16 of them) and the 16*BM staged x rows: acc and accz per
+// m-tile, lane layout of the MFMA result (rows 4*(lane/16) + e, column
+// lane % 16).  `xoff(r, c)` is the byte offset from `x` of chunk c of staged
+// row r (r < 16*BM, callers clamp it to a valid row).  Every thread of the
+// workgroup must call this (it holds workgroup barriers).
+template <int BITS, int BM, int CPG, typename XOff>
+__device__ __forceinline__ void qmm_accumulate(const uint32_t *__restrict__ w, const uint16_t *__restrict__ sp,
+                                               const uint16_t *__restrict__ bp_, const uint16_t *__restrict__ x,
+                                               uint32_t nrow, int Kc, int c0, int c1, XOff &&xoff,
+                                               unsigned char *smem, f32x4_t (&acc)[BM], f32x4_t (&accz)[BM]) {
+  constexpr int MR = 16 * BM;
   constexpr bool NIB = BITS == 8;
-  constexpr int P = NIB ? 3 : 7 - BITS;
   constexpr float kZc = NIB ? 272.0f : static_cast<float>(1 << BITS);   // z - kZc * s
   constexpr int GPB = kQmmKB / CPG;               // groups per K-block
-  extern __shared__ __align__(16) unsigned char smem[];
   unsigned char *xp = smem;                                       // [KB][MR][80]
   float *xsum = reinterpret_cast<float *>(smem + kQmmKB * MR * kQmmRow);   // [KB][MR]
-
   const int lane = threadIdx.x & (kWave - 1);
-  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int j = lane & 15, kb = lane >> 4;
-  const int64_t NB = (a.N + kQmmRowsPerWG - 1) / kQmmRowsPerWG;
-  const int64_t nb = blockIdx.x % NB;
-  const int sl = static_cast<int>(blockIdx.x / NB);
-  const int64_t n = nb * kQmmRowsPerWG + wid * 16 + j;
-  const uint32_t nrow = static_cast<uint32_t>(n < a.N ? n : a.N - 1);   // rows past N: not stored
-  const int Kc = a.K >> 5;
-  const int c0 = sl * a.cps;
-  const int c1 = min(Kc, c0 + a.cps);
   const uint32_t gpr = static_cast<uint32_t>(Kc / CPG);           // groups per row
   // 32-bit byte offsets from the arrays' scalar bases (the host keeps every
   // array under 4 GiB for this path)
@@ -158,7 +155,7 @@ __global__ __launch_bounds__(256) void qmm_kernel(QmmArgs a) {
   const uint32_t w_shift = NIB ? 0u : static_cast<uint32_t>((BITS * kb) & 3) * 8u;
   const PairConsts pk = pair_consts<NIB ? 4 : (BITS <= 6 ? BITS : 4)>();
 
-  f32x4_t acc[BM], accz[BM], D[BM], Dh[BM];
+  f32x4_t D[BM], Dh[BM];
 #pragma unroll
   for (int t = 0; t < BM; ++t) {
     acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -169,31 +166,30 @@ __global__ __launch_bounds__(256) void qmm_kernel(QmmArgs a) {
 
   for (int cb = c0; cb < c1; cb += kQmmKB) {
     // this block's weight windows, scales and biases first: their latency
-    // overlaps the staging (chunks past the slice re-read its last chunk)
+    // overlaps the staging (chunks past the range re-read its last chunk)
     uint32_t w0[kQmmKB], w1[kQmmKB];
     uint16_t sv[GPB], zv[GPB];
 #pragma unroll
     for (int cc = 0; cc < kQmmKB; ++cc) {
       const uint32_t c = static_cast<uint32_t>(min(cb + cc, c1 - 1));
       const uint32_t off = wlane + c * (BITS * 4);
-      w0[cc] = stream_load(byte_offset(a.w, off));
-      w1[cc] = stream_load(byte_offset(a.w, off + w_second));
+      w0[cc] = stream_load(byte_offset(w, off));
+      w1[cc] = stream_load(byte_offset(w, off + w_second));
     }
 #pragma unroll
     for (int gg = 0; gg < GPB; ++gg) {
       const uint32_t gi = static_cast<uint32_t>(min(cb + gg * CPG, c1 - 1)) / CPG;
-      sv[gg] = *byte_offset(a.s, (nrow * gpr + gi) * 2u);
-      zv[gg] = *byte_offset(a.b, (nrow * gpr + gi) * 2u);
+      sv[gg] = *byte_offset(sp, (nrow * gpr + gi) * 2u);
+      zv[gg] = *byte_offset(bp_, (nrow * gpr + gi) * 2u);
     }
     __syncthreads();                              // the previous block's LDS reads are done
-    // ---- stage x rows [0, MR) x chunks [cb, cb + KB) in pair order.  Rows
-    // past M and chunks past the slice restage a valid row / chunk: their
-    // products only reach outputs that are never stored or never consumed.
+    // ---- stage x rows [0, MR) x chunks [cb, cb + KB) in pair order.  Chunks
+    // past the range restage a valid chunk: their products are never used.
     for (int it = threadIdx.x; it < MR * kQmmKB; it += 256) {
       const int r = it / kQmmKB, cc = it - r * kQmmKB;
-      const int rr = min(r, a.M - 1), c = min(cb + cc, c1 - 1);
+      const int c = min(cb + cc, c1 - 1);
       uint32_t raw[16];
-      load_x_chunk(byte_offset(a.x, static_cast<uint32_t>(rr * a.K + c * 32) * 2u), raw);
+      load_x_chunk(byte_offset(x, xoff(r, c)), raw);
       float sum = 0.0f;
 #pragma unroll
       for (int q = 0; q < 16; ++q) sum = dot2_bf16(raw[q], 0x3F803F80u, sum);
@@ -217,10 +213,10 @@ __global__ __launch_bounds__(256) void qmm_kernel(QmmArgs a) {
       constexpr int cc = decltype(ccv)::value;
       constexpr bool first = cc % CPG == 0, last = cc % CPG == CPG - 1;
       if (cb + cc < c1) {                         // uniform; groups are whole
-        uint32_t bp[4], bh[4];
-        if constexpr (NIB) qmm_b_nibbles(w0[cc], w1[cc], pk, bp, bh);
-        else qmm_b_pairs<BITS>(w0[cc], w1[cc], w_shift, pk, bp);
-        const bf16x8_t B = __builtin_bit_cast(bf16x8_t, make_uint4(bp[0], bp[1], bp[2], bp[3]));
+        uint32_t bq[4], bh[4];
+        if constexpr (NIB) qmm_b_nibbles(w0[cc], w1[cc], pk, bq, bh);
+        else qmm_b_pairs<BITS>(w0[cc], w1[cc], w_shift, pk, bq);
+        const bf16x8_t B = __builtin_bit_cast(bf16x8_t, make_uint4(bq[0], bq[1], bq[2], bq[3]));
         const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < BM; ++t) {
@@ -255,6 +251,28 @@ __global__ __launch_bounds__(256) void qmm_kernel(QmmArgs a) {
       }
     });
   }
+}
+
+template <int BITS, int BM, int CPG>
+__global__ __launch_bounds__(256) void qmm_kernel(QmmArgs a) {
+  constexpr int MR = 16 * BM;                     // x rows per launch
+  constexpr int P = BITS == 8 ? 3 : 7 - BITS;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int j = lane & 15, kb = lane >> 4;
+  const int64_t NB = (a.N + kQmmRowsPerWG - 1) / kQmmRowsPerWG;
+  const int64_t nb = blockIdx.x % NB;
+  const int sl = static_cast<int>(blockIdx.x / NB);
+  const int64_t n = nb * kQmmRowsPerWG + wid * 16 + j;
+  const uint32_t nrow = static_cast<uint32_t>(n < a.N ? n : a.N - 1);   // rows past N: not stored
+  const int Kc = a.K >> 5;
+  const int c0 = sl * a.cps;
+  const int c1 = min(Kc, c0 + a.cps);
+  // rows past M restage row M - 1: their outputs are never stored
+  auto xoff = [&](int r, int c) { return static_cast<uint32_t>(min(r, a.M - 1) * a.K + c * 32) * 2u; };
+  f32x4_t acc[BM], accz[BM];
+  qmm_accumulate<BITS, BM, CPG>(a.w, a.s, a.b, a.x, nrow, Kc, c0, c1, xoff, smem, acc, accz);
 
   // ---- lane holds rows 4*kb + e of each m-tile, column n
   constexpr float kInvP = 1.0f / static_cast<float>(1 << P);
@@ -276,6 +294,115 @@ __global__ __launch_bounds__(256) void qmm_kernel(QmmArgs a) {
         }
       }
     }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Gathered matrix-core product (gather_qmv with many tokens per expert):
+// workgroup (e, nb) routes the pairs of expert e with the same ordered
+// ballot scan as the matvec gather, then takes their x vectors 64 at a time
+// through qmm_accumulate against W rows nb*64 .. +64 of expert e and
+// scatters the results to y[p].  Lists longer than 1024 pairs are served in
+// windows.
+// ----------------------------------------------------------------------------
+struct GatherQmmArgs {
+  const uint16_t *x;        // [Bx, M, K]
+  const uint32_t *w;        // [E, N, K*bits/32]
+  const uint16_t *s, *b;    // [E, N, K/g]
+  const uint32_t *lhs, *rhs;
+  int64_t P;
+  int64_t N;
+  int64_t Bx;
+  int K;
+  int M;
+  int out_f32;
+  void *y;                  // [P, M, N]
+};
+
+constexpr int kGqmmListMax = 1024;
+
+template <int BITS, int CPG>
+__global__ __launch_bounds__(256) void gather_qmm_kernel(GatherQmmArgs a) {
+  constexpr int BM = 4, MR = 64;
+  constexpr int P = BITS == 8 ? 3 : 7 - BITS;
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int list[kGqmmListMax];
+  __shared__ int xrow[kGqmmListMax];
+  __shared__ uint32_t rowoff[MR];                  // x byte offset of each staged row
+  __shared__ int wcnt[4];
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int kb = lane >> 4;
+  const int64_t NB = (a.N + kQmmRowsPerWG - 1) / kQmmRowsPerWG;
+  const int e = static_cast<int>(blockIdx.x / NB);
+  const int64_t nb = blockIdx.x % NB;
+  const int64_t n = nb * kQmmRowsPerWG + wid * 16 + (lane & 15);
+  const uint32_t nrow = static_cast<uint32_t>(n < a.N ? n : a.N - 1);
+  const int Kc = a.K >> 5;
+  const int64_t wrows = static_cast<int64_t>(e) * a.N;
+  const uint32_t *we = a.w + wrows * (static_cast<int64_t>(Kc) * BITS);
+  const uint16_t *se = a.s + wrows * (Kc / CPG);
+  const uint16_t *be = a.b + wrows * (Kc / CPG);
+
+  for (int win = 0;; win += kGqmmListMax) {
+    int seen = 0;
+    for (int64_t p0 = 0; p0 < a.P; p0 += 256) {
+      const int64_t p = p0 + threadIdx.x;
+      const bool hit = p < a.P && a.rhs[p] == static_cast<uint32_t>(e);
+      const unsigned long long mask = __ballot(hit);
+      if (lane == 0) wcnt[wid] = __popcll(mask);
+      __syncthreads();
+      int before = seen + __popcll(mask & ((1ull << lane) - 1ull));
+      int round = 0;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int cnt = wcnt[w];
+        before += (w < wid) ? cnt : 0;
+        round += cnt;
+      }
+      if (hit && before >= win && before < win + kGqmmListMax) {
+        list[before - win] = static_cast<int>(p);
+        xrow[before - win] = static_cast<int>(min(static_cast<int64_t>(a.lhs[p]), a.Bx - 1));
+      }
+      seen += round;
+      __syncthreads();
+    }
+    const int npairs = min(seen - win, kGqmmListMax);
+    if (npairs <= 0) return;                       // uniform
+    const int nvec = npairs * a.M;
+
+    for (int v0 = 0; v0 < nvec; v0 += MR) {
+      const int nv = min(MR, nvec - v0);
+      if (threadIdx.x < MR) {
+        const int vec = v0 + min(static_cast<int>(threadIdx.x), nv - 1);   // past nv: restage the last
+        const int pi = vec / a.M, m = vec - pi * a.M;
+        rowoff[threadIdx.x] = static_cast<uint32_t>((xrow[pi] * a.M + m) * a.K) * 2u;
+      }
+      __syncthreads();
+      auto xoff = [&](int r, int c) { return rowoff[r] + static_cast<uint32_t>(c) * 64u; };
+      f32x4_t acc[BM], accz[BM];
+      qmm_accumulate<BITS, BM, CPG>(we, se, be, a.x, nrow, Kc, 0, Kc, xoff, smem, acc, accz);
+
+      constexpr float kInvP = 1.0f / static_cast<float>(1 << P);
+#pragma unroll
+      for (int t = 0; t < BM; ++t) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = t * 16 + 4 * kb + q;
+          if (r < nv && n < a.N) {
+            const int vec = v0 + r;
+            const int pi = vec / a.M, m = vec - pi * a.M;
+            const float v = fmaf(acc[t][q], kInvP, accz[t][q]);
+            const int64_t o = (static_cast<int64_t>(list[pi]) * a.M + m) * a.N + n;
+            if (a.out_f32) static_cast<float *>(a.y)[o] = v;
+            else static_cast<uint16_t *>(a.y)[o] = f32_to_bf16(v);
+          }
+        }
+      }
+      __syncthreads();                             // rowoff / LDS reuse by the next slab
+    }
+    if (seen <= win + kGqmmListMax) return;
   }
 }
 

@@ -169,8 +169,11 @@ constexpr int64_t kGatherTiles = QMV_GATHER_TILES;
 constexpr int kGatherWaves = QMV_GATHER_WAVES;
 constexpr int kGatherDepth = QMV_GATHER_DEPTH;   // chunk steps in flight per wave
 // x vectors per pass over an expert's rows (fp32 staging is twice as wide)
+#ifndef QMV_GATHER_MV
+#define QMV_GATHER_MV 4           // x vectors per pass (fp32 staging: at most 2)
+#endif
 template <int BITS>
-constexpr int gather_mv() { return BITS <= 6 ? 4 : 2; }
+constexpr int gather_mv() { return BITS <= 6 ? QMV_GATHER_MV : (QMV_GATHER_MV < 2 ? QMV_GATHER_MV : 2); }
 // static LDS of the gather kernel: pair list, x rows, per-wave counts
 constexpr int64_t kGatherStaticLds = 2 * 4 * qmvk::kGatherListMax + 4 * kGatherWaves;
 
@@ -208,6 +211,30 @@ int launch_gather_t(const qmvk::GatherArgs &a0, int64_t E, hipStream_t st) {
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(E * tiles)), dim3(kGatherWaves * qmvk::kWave),
                      static_cast<size_t>(lds), st, a);
   return check_launch("gather_qmv");
+}
+
+#ifndef QMV_GATHER_QMM_MIN
+#define QMV_GATHER_QMM_MIN 12     // mean x vectors per expert for the matrix-core gather
+#endif
+
+template <int BITS, int CPG>
+int launch_gather_qmm_t(const qmvk::GatherQmmArgs &a, int64_t E, hipStream_t st) {
+  const int64_t NB = (a.N + qmvk::kQmmRowsPerWG - 1) / qmvk::kQmmRowsPerWG;
+  if (E * NB > 0x7FFFFFFF) return fail(QMV_EUNSUPPORTED, "gather_qmv: grid too large");
+  constexpr int lds = qmvk::qmm_lds_bytes<4>();
+  auto kern = qmvk::gather_qmm_kernel<BITS, CPG>;
+  allow_lds(kern, lds);
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(E * NB)), dim3(256), lds, st, a);
+  return check_launch("gather_qmv (matrix cores)");
+}
+
+template <int BITS>
+int launch_gather_qmm_g(int gshift, const qmvk::GatherQmmArgs &a, int64_t E, hipStream_t st) {
+  switch (gshift) {
+    case 0: return launch_gather_qmm_t<BITS, 1>(a, E, st);
+    case 1: return launch_gather_qmm_t<BITS, 2>(a, E, st);
+    default: return launch_gather_qmm_t<BITS, 4>(a, E, st);
+  }
 }
 
 template <int BITS>
@@ -658,6 +685,36 @@ int gather_qmv(const uint16_t *x, int64_t Bx, const uint32_t *w_q, const uint16_
   a.out_f32 = out_dtype == QMV_OUT_F32;
   a.y = y;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  // Many tokens per expert: the matrix-core gather (the matrix-core kernel
+  // addresses x, and each expert's W, scales and biases, with 32-bit offsets)
+  if (P * M >= QMV_GATHER_QMM_MIN * E && Bx * M * K * 2 < (int64_t(1) << 32) &&
+      N * K * bits / 8 < (int64_t(1) << 32)) {
+    qmvk::GatherQmmArgs g{};
+    g.x = x;
+    g.w = w_q;
+    g.s = scales;
+    g.b = biases;
+    g.lhs = lhs_indices;
+    g.rhs = rhs_indices;
+    g.P = P;
+    g.N = N;
+    g.Bx = Bx;
+    g.K = static_cast<int>(K);
+    g.M = static_cast<int>(M);
+    g.out_f32 = out_dtype == QMV_OUT_F32;
+    g.y = y;
+    const int gs = gshift_of(group_size);
+    int rc;
+    switch (bits) {
+      case 2: rc = launch_gather_qmm_g<2>(gs, g, E, st); break;
+      case 3: rc = launch_gather_qmm_g<3>(gs, g, E, st); break;
+      case 4: rc = launch_gather_qmm_g<4>(gs, g, E, st); break;
+      case 5: rc = launch_gather_qmm_g<5>(gs, g, E, st); break;
+      case 6: rc = launch_gather_qmm_g<6>(gs, g, E, st); break;
+      default: rc = launch_gather_qmm_g<8>(gs, g, E, st); break;
+    }
+    return rc ? rc : ok();
+  }
   int rc;
   switch (bits) {
     case 2: rc = launch_gather_t<2>(a, E, st); break;

@@ -92,7 +92,9 @@ int qmv_pack(const float *w, int64_t N, int64_t K, int group_size, int bits,
  *                  QMV_EUNSUPPORTED: make one eager call of that size on the
  *                  stream first.  Calls on one stream share its workspace
  *                  (stream order serializes them).
- * x: bf16 [M, K].  y: [M, N], bf16 or fp32 per out_dtype.  M >= 1.
+ * x: bf16 [M, K].  y: [M, N], bf16 or fp32 per out_dtype.  M >= 1.  With
+ * transpose = 1 and 12 or more rows of x the matrix cores are used (64-row
+ * slabs of x, W read once per slab).
  */
 int qmv(const uint16_t *x, const uint32_t *w_q, const uint16_t *scales,
         const uint16_t *biases, void *y, int64_t M, int64_t N, int64_t K,
@@ -138,7 +140,8 @@ int qmv_silu_gate_resid(const uint16_t *gate, const uint16_t *up,
  * [M, N].  Exactly one NULL is QMV_EINVAL.  sorted_indices = 1 promises rhs is
  * non-decreasing; it may make the call faster and never changes the results
  * (every output is computed with the same arithmetic either way).
- * transpose must be 1 (else QMV_EUNSUPPORTED).
+ * transpose must be 1 (else QMV_EUNSUPPORTED).  When the routed x vectors
+ * average 12 or more per expert (P*M >= 12*E) the matrix cores are used.
  */
 int gather_qmv(const uint16_t *x, int64_t Bx, const uint32_t *w_q,
                const uint16_t *scales, const uint16_t *biases, int64_t E,

@@ -307,7 +307,8 @@ def test_gather_moe_workload(dev):
 @pytest.mark.parametrize("bits", BITS)
 @pytest.mark.parametrize("M", (1, 2, 3))
 def test_gather_small(dev, bits, M):
-    E, N, K, g = 5, 70, 1152, 64
+    # fewer than 12 vectors per expert on average: the matvec gather
+    E, N, K, g = 7, 70, 1152, 64
     ew = _experts(E, N, K, bits, g, seed0=50 + bits)
     rng = np.random.default_rng(M * 10 + bits)
     Bx, P = 4, 23
@@ -326,15 +327,17 @@ def test_gather_small(dev, bits, M):
 
 @pytest.mark.parametrize("sorted_indices", (False, True))
 def test_gather_long_pair_lists(dev, sorted_indices):
-    """2500 pairs over 3 experts: one expert's list exceeds the 1024-pair
+    """2500 pairs over 300 experts (8.3 per expert on average: the matvec
+    gather), 1100 of them on expert 0: its list exceeds the 1024-pair
     routing window, so its rows are served in several windows."""
-    E, N, K, g, bits = 3, 48, 256, 64, 4
+    E, N, K, g, bits = 300, 48, 256, 64, 4
     ew = _experts(E, N, K, bits, g, seed0=77)
     rng = np.random.default_rng(5)
     Bx, P = 40, 2500
     x = synth.activation_bf16((Bx, 1, K), seed=6)
     lhs = rng.integers(0, Bx, P).astype(np.uint32)
-    rhs = rng.choice(E, P, p=[0.7, 0.2, 0.1]).astype(np.uint32)
+    rhs = rng.integers(1, E, P).astype(np.uint32)
+    rhs[rng.choice(P, 1100, replace=False)] = 0
     if sorted_indices:
         perm = np.argsort(rhs, kind="stable")
         lhs, rhs = lhs[perm], rhs[perm]
