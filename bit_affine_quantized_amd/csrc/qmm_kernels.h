@@ -18,7 +18,7 @@
 // byte-aligned window of the chunk, and x is staged once per workgroup in the
 // same order.
 //
-// A workgroup (4 waves) covers 64 W rows (16 per wave) by up to 64 x rows
+// A workgroup (kQmmWaves waves) covers 16 W rows per wave by up to 64 x rows
 // (BM m-tiles) over a slice of K; x is staged in LDS 8 chunks at a time.  A
 // slice's fp32 result goes to y directly, or, with several slices, to the
 // workspace, whose slices are then added in order by a second kernel.
@@ -47,9 +47,14 @@ struct QmmArgs {
   int out_f32;
 };
 
+#ifndef QMV_QMM_WAVES
+#define QMV_QMM_WAVES 4
+#endif
 constexpr int kQmmKB = 8;          // chunks per staged K-block
 constexpr int kQmmRow = 80;        // bytes per staged (x row, chunk): 64 B of pairs + pad
-constexpr int kQmmRowsPerWG = 64;  // W rows per workgroup
+constexpr int kQmmWaves = QMV_QMM_WAVES;         // waves per workgroup, 16 W rows each
+constexpr int kQmmThreads = kQmmWaves * kWave;
+constexpr int kQmmRowsPerWG = 16 * kQmmWaves;    // W rows per workgroup
 
 template <int BM>
 constexpr int qmm_lds_bytes() {
@@ -167,26 +172,28 @@ __device__ __forceinline__ void qmm_accumulate(const uint32_t *__restrict__ w, c
   for (int cb = c0; cb < c1; cb += kQmmKB) {
     // this block's weight windows, scales and biases first: their latency
     // overlaps the staging (chunks past the range re-read its last chunk)
-    uint32_t w0[kQmmKB], w1[kQmmKB];
-    uint16_t sv[GPB], zv[GPB];
+    uint32_t wa[kQmmKB], wb[kQmmKB];
+    uint16_t sa[GPB], za[GPB];
 #pragma unroll
     for (int cc = 0; cc < kQmmKB; ++cc) {
       const uint32_t c = static_cast<uint32_t>(min(cb + cc, c1 - 1));
       const uint32_t off = wlane + c * (BITS * 4);
-      w0[cc] = stream_load(byte_offset(w, off));
-      w1[cc] = stream_load(byte_offset(w, off + w_second));
+      wa[cc] = stream_load(byte_offset(w, off));
+      wb[cc] = stream_load(byte_offset(w, off + w_second));
     }
 #pragma unroll
     for (int gg = 0; gg < GPB; ++gg) {
       const uint32_t gi = static_cast<uint32_t>(min(cb + gg * CPG, c1 - 1)) / CPG;
-      sv[gg] = *byte_offset(sp, (nrow * gpr + gi) * 2u);
-      zv[gg] = *byte_offset(bp_, (nrow * gpr + gi) * 2u);
+      sa[gg] = *byte_offset(sp, (nrow * gpr + gi) * 2u);
+      za[gg] = *byte_offset(bp_, (nrow * gpr + gi) * 2u);
     }
     __syncthreads();                              // the previous block's LDS reads are done
     // ---- stage x rows [0, MR) x chunks [cb, cb + KB) in pair order.  Chunks
     // past the range restage a valid chunk: their products are never used.
-    for (int it = threadIdx.x; it < MR * kQmmKB; it += 256) {
-      const int r = it / kQmmKB, cc = it - r * kQmmKB;
+    // Consecutive threads take consecutive rows of one chunk: their 16-byte
+    // LDS stores are 80 bytes apart (no bank conflicts), as are the sums.
+    for (int it = threadIdx.x; it < MR * kQmmKB; it += kQmmThreads) {
+      const int cc = it / MR, r = it - cc * MR;
       const int c = min(cb + cc, c1 - 1);
       uint32_t raw[16];
       load_x_chunk(byte_offset(x, xoff(r, c)), raw);
@@ -214,8 +221,8 @@ __device__ __forceinline__ void qmm_accumulate(const uint32_t *__restrict__ w, c
       constexpr bool first = cc % CPG == 0, last = cc % CPG == CPG - 1;
       if (cb + cc < c1) {                         // uniform; groups are whole
         uint32_t bq[4], bh[4];
-        if constexpr (NIB) qmm_b_nibbles(w0[cc], w1[cc], pk, bq, bh);
-        else qmm_b_pairs<BITS>(w0[cc], w1[cc], w_shift, pk, bq);
+        if constexpr (NIB) qmm_b_nibbles(wa[cc], wb[cc], pk, bq, bh);
+        else qmm_b_pairs<BITS>(wa[cc], wb[cc], w_shift, pk, bq);
         const bf16x8_t B = __builtin_bit_cast(bf16x8_t, make_uint4(bq[0], bq[1], bq[2], bq[3]));
         const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -229,8 +236,8 @@ __device__ __forceinline__ void qmm_accumulate(const uint32_t *__restrict__ w, c
           }
         }
         if constexpr (last) {                     // fold the group
-          const float s = bf16_to_f32(sv[cc / CPG]);
-          const float zc = fmaf(-kZc, s, bf16_to_f32(zv[cc / CPG]));
+          const float s = bf16_to_f32(sa[cc / CPG]);
+          const float zc = fmaf(-kZc, s, bf16_to_f32(za[cc / CPG]));
 #pragma unroll
           for (int t = 0; t < BM; ++t) {
             float4 xg = *reinterpret_cast<const float4 *>(xsum + (cc - CPG + 1) * MR + t * 16 + 4 * kb);
@@ -254,7 +261,7 @@ __device__ __forceinline__ void qmm_accumulate(const uint32_t *__restrict__ w, c
 }
 
 template <int BITS, int BM, int CPG>
-__global__ __launch_bounds__(256) void qmm_kernel(QmmArgs a) {
+__global__ __launch_bounds__(kQmmThreads) void qmm_kernel(QmmArgs a) {
   constexpr int MR = 16 * BM;                     // x rows per launch
   constexpr int P = BITS == 8 ? 3 : 7 - BITS;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -322,14 +329,14 @@ struct GatherQmmArgs {
 constexpr int kGqmmListMax = 1024;
 
 template <int BITS, int CPG>
-__global__ __launch_bounds__(256) void gather_qmm_kernel(GatherQmmArgs a) {
+__global__ __launch_bounds__(kQmmThreads) void gather_qmm_kernel(GatherQmmArgs a) {
   constexpr int BM = 4, MR = 64;
   constexpr int P = BITS == 8 ? 3 : 7 - BITS;
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int list[kGqmmListMax];
   __shared__ int xrow[kGqmmListMax];
   __shared__ uint32_t rowoff[MR];                  // x byte offset of each staged row
-  __shared__ int wcnt[4];
+  __shared__ int wcnt[kQmmWaves];
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -346,24 +353,47 @@ __global__ __launch_bounds__(256) void gather_qmm_kernel(GatherQmmArgs a) {
   const uint16_t *be = a.b + wrows * (Kc / CPG);
 
   for (int win = 0;; win += kGqmmListMax) {
+    // ---- ordered list of the pairs routed to e, ranks [win, win + max).
+    // Each thread takes a contiguous run of kRun pairs (its loads issued
+    // together), counts its hits, and a block-wide exclusive scan of the
+    // counts gives its first rank: ranks follow p whatever the order of rhs.
+    constexpr int kRun = 16;
     int seen = 0;
-    for (int64_t p0 = 0; p0 < a.P; p0 += 256) {
-      const int64_t p = p0 + threadIdx.x;
-      const bool hit = p < a.P && a.rhs[p] == static_cast<uint32_t>(e);
-      const unsigned long long mask = __ballot(hit);
-      if (lane == 0) wcnt[wid] = __popcll(mask);
+    for (int64_t base = 0; base < a.P; base += static_cast<int64_t>(kQmmThreads) * kRun) {
+      const int64_t p0 = base + static_cast<int64_t>(threadIdx.x) * kRun;
+      uint32_t hits = 0;
+#pragma unroll
+      for (int r = 0; r < kRun; ++r) {
+        const int64_t p = p0 + r;
+        if (p < a.P && a.rhs[p] == static_cast<uint32_t>(e)) hits |= 1u << r;
+      }
+      const int cnt = __popc(hits);
+      // inclusive scan over the wave, then over the waves
+      int incl = cnt;
+#pragma unroll
+      for (int d = 1; d < kWave; d <<= 1) {
+        const int v = __shfl_up(incl, d, kWave);
+        if (lane >= d) incl += v;
+      }
+      if (lane == kWave - 1) wcnt[wid] = incl;
       __syncthreads();
-      int before = seen + __popcll(mask & ((1ull << lane) - 1ull));
+      int before = seen + incl - cnt;
       int round = 0;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const int cnt = wcnt[w];
-        before += (w < wid) ? cnt : 0;
-        round += cnt;
+      for (int w = 0; w < kQmmWaves; ++w) {
+        const int c = wcnt[w];
+        before += (w < wid) ? c : 0;
+        round += c;
       }
-      if (hit && before >= win && before < win + kGqmmListMax) {
-        list[before - win] = static_cast<int>(p);
-        xrow[before - win] = static_cast<int>(min(static_cast<int64_t>(a.lhs[p]), a.Bx - 1));
+      while (hits) {
+        const int r = __ffs(hits) - 1;
+        hits &= hits - 1u;
+        if (before >= win && before < win + kGqmmListMax) {
+          const int64_t p = p0 + r;
+          list[before - win] = static_cast<int>(p);
+          xrow[before - win] = static_cast<int>(min(static_cast<int64_t>(a.lhs[p]), a.Bx - 1));
+        }
+        ++before;
       }
       seen += round;
       __syncthreads();

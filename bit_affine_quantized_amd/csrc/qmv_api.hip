@@ -224,7 +224,7 @@ int launch_gather_qmm_t(const qmvk::GatherQmmArgs &a, int64_t E, hipStream_t st)
   constexpr int lds = qmvk::qmm_lds_bytes<4>();
   auto kern = qmvk::gather_qmm_kernel<BITS, CPG>;
   allow_lds(kern, lds);
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(E * NB)), dim3(256), lds, st, a);
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(E * NB)), dim3(qmvk::kQmmThreads), lds, st, a);
   return check_launch("gather_qmv (matrix cores)");
 }
 
@@ -392,7 +392,7 @@ int launch_qmm_t(const qmvk::QmmArgs &a0, hipStream_t st) {
   constexpr int lds = qmvk::qmm_lds_bytes<BM>();
   auto kern = qmvk::qmm_kernel<BITS, BM, CPG>;
   allow_lds(kern, lds);
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(NB * S)), dim3(256), lds, st, a);
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(NB * S)), dim3(qmvk::kQmmThreads), lds, st, a);
   if (int rc = check_launch("qmv (matrix cores)")) return rc;
   if (S > 1) {
     const int64_t outs = static_cast<int64_t>(a.M) * a.N;
