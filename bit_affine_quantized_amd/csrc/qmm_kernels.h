@@ -61,28 +61,6 @@ constexpr int qmm_lds_bytes() {
   return kQmmKB * 16 * BM * kQmmRow + kQmmKB * 16 * BM * 4;
 }
 
-// The 8 codes 8i..8i+7 of a chunk (lane group i), as a 64-bit window whose
-// bits [0, 8b) hold them in order.  b <= 6: the window is byte-aligned at
-// byte b*i of the chunk; a second word is read only when the codes cross a
-// word (otherwise the first word is read again: no read past the chunk).
-template <int BITS>
-__device__ __forceinline__ void qmm_load_window(const uint32_t *__restrict__ chunk, int i,
-                                                uint32_t &w0, uint32_t &w1, uint32_t &shift) {
-  if constexpr (BITS == 8) {
-    const u32x2_t v = stream_load(reinterpret_cast<const u32x2_t *>(chunk) + i);
-    w0 = v.x;
-    w1 = v.y;
-    shift = 0;
-  } else {
-    const int byte0 = BITS * i;
-    const int wd = byte0 >> 2;
-    const int second = ((byte0 & 3) + BITS > 4) ? 1 : 0;
-    w0 = stream_load(chunk + wd);
-    w1 = stream_load(chunk + wd + second);
-    shift = static_cast<uint32_t>(byte0 & 3) * 8u;
-  }
-}
-
 // Magic-bf16 B operand (4 dwords = 8 bf16) from the lane's window: pair j
 // holds codes j (low half) and j + 4 (high half).
 template <int BITS>
@@ -153,7 +131,11 @@ __device__ __forceinline__ void qmm_accumulate(const uint32_t *__restrict__ w, c
   const int j = lane & 15, kb = lane >> 4;
   const uint32_t gpr = static_cast<uint32_t>(Kc / CPG);           // groups per row
   // 32-bit byte offsets from the arrays' scalar bases (the host keeps every
-  // array under 4 GiB for this path)
+  // array under 4 GiB for this path).  The lane's window of 8 codes
+  // (8kb..8kb+7) starts at byte b*kb of a chunk (8-bit codes: at word 2kb);
+  // a second word is read only when the codes cross a word boundary
+  // (otherwise the first word is read again: never past the chunk), and
+  // w_shift aligns the window to bit 0.
   const uint32_t wlane = nrow * static_cast<uint32_t>(Kc * BITS * 4) +
                          (NIB ? static_cast<uint32_t>(kb) * 8u : static_cast<uint32_t>(BITS * kb) & ~3u);
   const uint32_t w_second = NIB ? 4u : ((((BITS * kb) & 3) + BITS > 4) ? 4u : 0u);

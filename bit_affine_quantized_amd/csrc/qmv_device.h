@@ -186,16 +186,6 @@ __device__ __forceinline__ T stream_load(const T *p) {
 #endif
 }
 
-// An index that is the same in every lane, made visibly wave-uniform so that
-// addresses built from it stay scalar.  (Readfirstlane on the index, not on a
-// pointer: a pointer rebuilt from an integer loses its global address space
-// and turns the loads into flat loads, which also stall LDS waits.)
-__device__ __forceinline__ int64_t uniform_index(int64_t i) {
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(i));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(i) >> 32));
-  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
-}
-
 // base + a 32-bit byte offset: lets the compiler use the global_load
 // "saddr + 32-bit voffset" form when the base is wave-uniform.
 template <typename T>
