@@ -156,18 +156,19 @@ int64_t qmv_lds_bytes(int bits, int mv, int64_t K) {
 #define QMV_GATHER_WAVES 4
 #endif
 #ifndef QMV_GATHER_DEPTH
-#define QMV_GATHER_DEPTH 4
+#define QMV_GATHER_DEPTH 2
 #endif
-#ifndef QMV_GATHER_RPW
-#define QMV_GATHER_RPW 1
+#ifndef QMV_GATHER_CPL
+#define QMV_GATHER_CPL 1          // chunks per lane per step (at most 2 for 5- to 8-bit codes)
 #endif
 #ifndef QMV_GATHER_TILES
 #define QMV_GATHER_TILES 2048     // target workgroups over the whole expert stack
 #endif
-constexpr int kGatherRpw = QMV_GATHER_RPW;
+template <int BITS>
+constexpr int gather_cpl() { return BITS <= 4 ? QMV_GATHER_CPL : (QMV_GATHER_CPL < 2 ? QMV_GATHER_CPL : 2); }
 constexpr int64_t kGatherTiles = QMV_GATHER_TILES;
 constexpr int kGatherWaves = QMV_GATHER_WAVES;
-constexpr int kGatherDepth = QMV_GATHER_DEPTH;   // chunk steps in flight per wave
+constexpr int kGatherDepth = QMV_GATHER_DEPTH;   // steps in flight per wave
 // x vectors per pass over an expert's rows (fp32 staging is twice as wide)
 #ifndef QMV_GATHER_MV
 #define QMV_GATHER_MV 4           // x vectors per pass (fp32 staging: at most 2)
@@ -188,8 +189,8 @@ int launch_gather_t(const qmvk::GatherArgs &a0, int64_t E, hipStream_t st) {
   // yet enough rows per tile that routing and x staging are paid once per
   // many rows; the parked row sums (tile_rows * MV floats) must fit in LDS
   // beside x and the pair list.  (64x2048x2048 4-bit, 128 pairs on MI355X:
-  // 512 tiles of 2-row waves 67 us, 2048 tiles of 1-row waves 45 us.)
-  const int64_t unit = kGatherWaves * kGatherRpw;
+  // 2048 tiles measured 7-10% ahead of 1024 or 4096.)
+  const int64_t unit = kGatherWaves * qmvk::kGatherRows;
   int64_t tile_rows = (a.N * E + kGatherTiles - 1) / kGatherTiles;
   tile_rows = ((tile_rows + unit - 1) / unit) * unit;
   const int64_t n_round = ((a.N + unit - 1) / unit) * unit;
@@ -206,7 +207,7 @@ int launch_gather_t(const qmvk::GatherArgs &a0, int64_t E, hipStream_t st) {
   a.tiles = static_cast<int>(tiles);
   a.tile_rows = static_cast<int>(tile_rows);
   a.res_offset = static_cast<int>(lds_x);
-  auto kern = qmvk::gather_kernel<BITS, kGatherRpw, kGatherMv, kGatherWaves, kGatherDepth>;
+  auto kern = qmvk::gather_kernel<BITS, kGatherMv, kGatherWaves, kGatherDepth, gather_cpl<BITS>()>;
   allow_lds(kern, lds);
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(E * tiles)), dim3(kGatherWaves * qmvk::kWave),
                      static_cast<size_t>(lds), st, a);
@@ -668,6 +669,9 @@ int gather_qmv(const uint16_t *x, int64_t Bx, const uint32_t *w_q, const uint16_
     return fail(QMV_EUNSUPPORTED, "gather_qmv: K=%lld too large", (long long)K);
   if (M > (int64_t(1) << 20) || P > (int64_t(1) << 30))
     return fail(QMV_EUNSUPPORTED, "gather_qmv: M or P too large");
+  // one expert's words, scales and biases are addressed with 32-bit offsets
+  if (N * (K / 32) * bits * 4 + 64 * (K / 32) * bits * 4 >= (int64_t(1) << 31))
+    return fail(QMV_EUNSUPPORTED, "gather_qmv: one expert's packed weight must be under 2 GiB");
   qmvk::GatherArgs a{};
   a.x = x;
   a.w = w_q;

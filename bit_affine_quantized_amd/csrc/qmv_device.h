@@ -212,6 +212,31 @@ __device__ __forceinline__ void load_chunk(const uint32_t *__restrict__ p, uint3
   }
 }
 
+// The same chunk through a buffer resource: `off` is the chunk's byte offset
+// from the resource base, held in the VGPR operand.  The hardware range
+// check covers that operand: a chunk at or past the resource's byte count
+// reads as zeros.  Dword 3 of a raw gfx9 resource: 32-bit data format, no
+// swizzle, no index stride.
+constexpr int kBufferDword3 = 0x00020000;
+constexpr int kBufferNt = QMV_NT_LOADS ? 2 : 0;   // cache policy of the weight words
+
+template <int BITS>
+__device__ __forceinline__ void buffer_load_chunk(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t (&w)[BITS]) {
+  if constexpr (BITS == 4 || BITS == 8) {
+#pragma unroll
+    for (int h = 0; h < BITS / 4; ++h) {
+      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * h, 0, kBufferNt);
+      w[4 * h] = v.x; w[4 * h + 1] = v.y; w[4 * h + 2] = v.z; w[4 * h + 3] = v.w;
+    }
+  } else if constexpr (BITS == 2) {
+    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kBufferNt);
+    w[0] = v.x; w[1] = v.y;
+  } else {
+#pragma unroll
+    for (int d = 0; d < BITS; ++d) w[d] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 4 * d, 0, kBufferNt);
+  }
+}
+
 // ----------------------------------------------------------------------------
 // Wave reduction of V values per lane (V a power of two, V <= 64).  A
 // transposing butterfly over lane bits 5, 4, 3, ...: at each step the lanes

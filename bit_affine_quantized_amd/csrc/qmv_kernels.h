@@ -153,14 +153,13 @@ struct ChunkStep {
 };
 
 // ----------------------------------------------------------------------------
-// One 32-code chunk of RPW rows against MV staged x vectors (chunk c of the
-// row; the caller has checked c < Kc).
+// One 32-code chunk of RPW rows against MV staged x vectors; `chunk` is the
+// staged chunk (layout above) and the caller has checked that it exists.
 // ----------------------------------------------------------------------------
 template <int BITS, int RPW, int MV, bool PAIR>
-__device__ __forceinline__ void accumulate_chunk(const ChunkStep<BITS, RPW> &st, const unsigned char *lds,
-                                                 int nv, int c, PairConsts pk,
+__device__ __forceinline__ void accumulate_chunk(const ChunkStep<BITS, RPW> &st, const unsigned char *chunk,
+                                                 int nv, PairConsts pk,
                                                  float (&acc)[RPW][MV], float (&accz)[RPW][MV]) {
-  const unsigned char *chunk = lds + c * chunk_stride<PAIR, MV>();
   const float *sums = reinterpret_cast<const float *>(chunk + MV * vec_bytes<PAIR>());
   if constexpr (PAIR && MV == 1) {
     // one x vector: keep its pairs in registers, build one row's pairs at a time
@@ -324,7 +323,7 @@ struct WaveEngine {
                                           const unsigned char *lds, int nv) {
     const int c = step * kWave + lane;
     if (c >= Kc) return;
-    accumulate_chunk<BITS, RPW, MV, PAIR>(st, lds, nv, c, pk, acc, accz);
+    accumulate_chunk<BITS, RPW, MV, PAIR>(st, lds + c * chunk_stride<PAIR, MV>(), nv, pk, acc, accz);
   }
 
   // Issue the first two steps' loads (before x staging); with one step the
@@ -461,6 +460,46 @@ __global__ __launch_bounds__(WPB * kWave) void qmv_kernel(QmvArgs a) {
 }
 
 // ----------------------------------------------------------------------------
+// One chunk of one row against NV staged x vectors (bf16 pairs), taken a
+// quad of pairs at a time: the quad's 4 pairs are built, then each vector's
+// matching 16 bytes of x are read and folded into its own dot chain.  Only a
+// quad's pairs and x are live at once (instead of all 16 pairs and a whole
+// vector), and the NV chains interleave.
+// ----------------------------------------------------------------------------
+template <int BITS, int MV, int NV>
+__device__ __forceinline__ void gather_chunk_pairs(const uint32_t (&w)[BITS], uint16_t sb, uint16_t bb,
+                                                   const unsigned char *chunk, PairConsts pk,
+                                                   float (&acc)[1][MV], float (&accz)[1][MV]) {
+  float d[NV];
+  static_for<0, 4>([&](auto qq) {
+    constexpr int q = decltype(qq)::value;
+    uint32_t p[4];
+    static_for<0, 4>([&](auto jj) {
+      constexpr int j = decltype(jj)::value;
+      p[j] = make_pair<BITS, 4 * q + j>(w, pk);
+    });
+#pragma unroll
+    for (int m = 0; m < NV; ++m) {
+      const uint4 xv = *reinterpret_cast<const uint4 *>(chunk + m * 64 + q * 16);
+      float t = q == 0 ? 0.0f : d[m];
+      t = dot2_bf16(p[0], xv.x, t);
+      t = dot2_bf16(p[1], xv.y, t);
+      t = dot2_bf16(p[2], xv.z, t);
+      d[m] = dot2_bf16(p[3], xv.w, t);
+    }
+    __builtin_amdgcn_sched_barrier(0);   // keep the next quad's reads below this one
+  });
+  const float *sums = reinterpret_cast<const float *>(chunk + MV * 64);
+  const float s = bf16_to_f32(sb);
+  const float zc = fmaf(-static_cast<float>(1 << BITS), s, bf16_to_f32(bb));   // z - 2^b s
+#pragma unroll
+  for (int m = 0; m < NV; ++m) {
+    acc[0][m] = fmaf(s, d[m], acc[0][m]);
+    accz[0][m] = fmaf(zc, sums[m], accz[0][m]);
+  }
+}
+
+// ----------------------------------------------------------------------------
 // Gather kernel (mlx.core.gather_qmm; quantized.h adjust_matrix_offsets):
 // y[p] = x[lhs[p]] @ W[rhs[p]]^T.
 //
@@ -472,10 +511,16 @@ __global__ __launch_bounds__(WPB * kWave) void qmv_kernel(QmvArgs a) {
 // so sorted and unsorted indices run identical arithmetic for every output.
 // Lists longer than kGatherListMax are processed in windows.
 //
-// Each wave streams its share of the tile (row groups of RPW rows) through a
-// DEPTH-deep software pipeline that runs across row groups; loads are
-// branch-free (clamped), and a row group's partial sums are reduced and
-// stored as soon as its last chunk is in.
+// Rows are cut into segments of 8 lanes: a wave step covers 8 rows, and lane
+// u of a row's segment takes chunks u, u + 8, ..., u + 8 (CPL - 1) of the
+// step's K range, so each of the CPL loads reads 8 x (chunk bytes) contiguous
+// bytes of every row.  A row's partial sums meet in a 3-level DPP reduction
+// inside its segment once per row group, not once per step: with few x
+// vectors per expert the per-row reduction and bookkeeping of a
+// one-row-per-wave layout cost as much as the dot products.  Each wave
+// streams its row groups (tile_rows / (waves x 8) of them, each K / (8 x 32
+// CPL) steps long) through a DEPTH-deep load ring; loads are branch-free
+// (clamped).
 // ----------------------------------------------------------------------------
 struct GatherArgs {
   const uint16_t *x;        // [Bx, M, K]
@@ -489,18 +534,25 @@ struct GatherArgs {
   int M;
   int gshift;
   int tiles;                // row tiles per expert
-  int tile_rows;            // rows per tile (a multiple of waves * RPW)
+  int tile_rows;            // rows per tile (a multiple of waves * 8)
   int res_offset;           // LDS bytes before the parked row sums
   int out_f32;
   void *y;                  // [P, M, N]
 };
 
 constexpr int kGatherListMax = 1024;   // pairs of one expert per window
+constexpr int kGatherSeg = 8;          // lanes per row
+constexpr int kGatherRows = kWave / kGatherSeg;   // rows per wave step
 
-template <int BITS, int RPW, int MV, int GW, int DEPTH>
-__global__ __launch_bounds__(GW * kWave) void gather_kernel(GatherArgs a) {
+#ifndef QMV_GATHER_WPE
+#define QMV_GATHER_WPE 1
+#endif
+template <int BITS, int MV, int GW, int DEPTH, int CPL>
+__global__ __launch_bounds__(GW * kWave) __attribute__((amdgpu_waves_per_eu(QMV_GATHER_WPE)))
+void gather_kernel(GatherArgs a) {
   constexpr bool PAIR = BITS <= 6;
   constexpr int NT = GW * kWave;
+  constexpr int SEG = kGatherSeg, R = kGatherRows, KS = SEG * CPL;
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int list[kGatherListMax];    // pair index p, in increasing order
   __shared__ int xrow[kGatherListMax];    // its x batch row lhs[p]
@@ -510,71 +562,70 @@ __global__ __launch_bounds__(GW * kWave) void gather_kernel(GatherArgs a) {
   const int tile = blockIdx.x - e * a.tiles;
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int u = lane & (SEG - 1), rl = lane / SEG;
   const int Kc = a.K >> 5;
-  const int nsteps = (Kc + kWave - 1) / kWave;
+  const int nks = (Kc + KS - 1) / KS;                        // steps per row group
   const int64_t wstride = static_cast<int64_t>(Kc) * BITS;   // words per row
   const int64_t gstride = Kc >> a.gshift;                    // groups per row
-  const int64_t row_base = static_cast<int64_t>(tile) * a.tile_rows + wid * RPW;
-  const int RG = a.tile_rows / (GW * RPW);
-  const int T = RG * nsteps;
+  const int64_t row_base = static_cast<int64_t>(tile) * a.tile_rows + wid * R;
+  const int RG = a.tile_rows / (GW * R);
+  const int T = RG * nks;
   const uint32_t *we = a.w + static_cast<int64_t>(e) * a.N * wstride;
   const uint16_t *se = a.s + static_cast<int64_t>(e) * a.N * gstride;
   const uint16_t *be = a.b + static_cast<int64_t>(e) * a.N * gstride;
   const PairConsts pk = pair_consts<BITS>();
-  // Row sums are parked in LDS (RG * RPW * MV floats per wave) and written
-  // out after the row loop: global stores inside it would share the memory
+  // Row sums are parked in LDS (RG * R * MV floats per wave) and written out
+  // after the row loop: global stores inside it would share the memory
   // counter with the weight loads and force full waits on every step.
-  float *res = reinterpret_cast<float *>(smem + a.res_offset) + wid * (RG * RPW * MV);
+  float *res = reinterpret_cast<float *>(smem + a.res_offset) + wid * (RG * R * MV);
 
-  // ---- the weight stream: RG row groups x nsteps chunk steps per wave, with
-  // DEPTH steps in flight.  Scalar cursors point at the current row group's
-  // first row and advance by GW*RPW rows; rows past N and steps past the
-  // wave's last read the (hot) head of x instead and are never consumed.
-  const uint32_t dummy_off = static_cast<uint32_t>(min(lane * 16, a.K * 2 - 32));
-  const int64_t wrow_bytes = wstride * 4, grow_bytes = gstride * 2;
-  const int64_t left0 = a.N - row_base;
-  const int rows_left0 = static_cast<int>(left0 < 0x40000000 ? left0 : 0x40000000);
-  const unsigned char *w0 = reinterpret_cast<const unsigned char *>(we) + row_base * wrow_bytes;
-  const unsigned char *s0 = reinterpret_cast<const unsigned char *>(se) + row_base * grow_bytes;
-  const unsigned char *b0 = reinterpret_cast<const unsigned char *>(be) + row_base * grow_bytes;
-  const unsigned char *wcur = w0, *scur = s0, *bcur = b0;
-  int l_t = 0, l_step = 0, rows_left = rows_left0;
-  auto load_next = [&](ChunkStep<BITS, RPW> &st) {
-    const bool live = l_t < T;
-    const uint32_t c = static_cast<uint32_t>(min(l_step * kWave + lane, Kc - 1));
-    const uint32_t gi = c >> a.gshift;
+  // ---- the weight stream, through buffer resources that span this
+  // expert's rows: a load past its last row returns zeros instead of
+  // reading out of bounds, so the loads need no clamps or selects.  (Rows
+  // past N, chunks past a row's end and steps past the wave's last are
+  // loaded but never consumed.)  Every offset is in the VGPR operand, which
+  // the range check covers.  Lane (rl, u) reads chunk u of row rl of the
+  // step; the scalar step offsets advance by one K range per step and to
+  // the next row group (GW*R rows on) on a wrap.
+  const uint32_t cb = BITS * 4;                              // bytes per chunk
+  const uint32_t wrow_b = static_cast<uint32_t>(wstride * 4), grow_b = static_cast<uint32_t>(gstride * 2);
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t *>(we), 0, static_cast<int>(a.N * wrow_b), kBufferDword3);
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(se), 0, static_cast<int>(a.N * grow_b), kBufferDword3);
+  const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(be), 0, static_cast<int>(a.N * grow_b), kBufferDword3);
+  const uint32_t lrow = static_cast<uint32_t>(row_base) + rl;
+  const uint32_t wlane = lrow * wrow_b + u * cb;
+  const uint32_t glane = lrow * grow_b + (static_cast<uint32_t>(u) >> a.gshift) * 2;
+  const uint32_t w_wrap = GW * R * wrow_b - (nks - 1) * (KS * cb);
+  const uint32_t g_wrap = GW * R * grow_b - (nks - 1) * ((KS >> a.gshift) * 2);
+  uint32_t w_step = 0, g_step = 0;
+  int l_ks = 0;
+  auto load_next = [&](ChunkStep<BITS, CPL> &st) {
 #pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-      const bool ok = live && r < rows_left;
-      const unsigned char *wp = ok ? wcur + r * wrow_bytes : reinterpret_cast<const unsigned char *>(a.x);
-      const unsigned char *sp = ok ? scur + r * grow_bytes : reinterpret_cast<const unsigned char *>(a.x);
-      const unsigned char *bp = ok ? bcur + r * grow_bytes : reinterpret_cast<const unsigned char *>(a.x);
-      load_chunk<BITS>(reinterpret_cast<const uint32_t *>(wp + (ok ? c * (BITS * 4) : dummy_off)), st.w[r]);
-      st.s[r] = *reinterpret_cast<const uint16_t *>(sp + (ok ? gi * 2 : dummy_off));
-      st.b[r] = *reinterpret_cast<const uint16_t *>(bp + (ok ? gi * 2 : dummy_off));
+    for (int i = 0; i < CPL; ++i) {
+      buffer_load_chunk<BITS>(wrs, wlane + (w_step + i * SEG * cb), st.w[i]);
+      const uint32_t go = glane + (g_step + ((i * SEG) >> a.gshift) * 2);
+      st.s[i] = __builtin_amdgcn_raw_buffer_load_b16(srs, go, 0, 0);
+      st.b[i] = __builtin_amdgcn_raw_buffer_load_b16(brs, go, 0, 0);
     }
     // advance by selects (increments in branches end up in scratch)
-    const bool wrap = l_step + 1 == nsteps;
-    l_t += 1;
-    l_step = wrap ? 0 : l_step + 1;
-    rows_left -= wrap ? GW * RPW : 0;
-    wcur += wrap ? (GW * RPW) * wrow_bytes : 0;
-    scur += wrap ? (GW * RPW) * grow_bytes : 0;
-    bcur += wrap ? (GW * RPW) * grow_bytes : 0;
+    const bool wrap = l_ks + 1 == nks;
+    l_ks = wrap ? 0 : l_ks + 1;
+    w_step += wrap ? w_wrap : KS * cb;
+    g_step += wrap ? g_wrap : (KS >> a.gshift) * 2;
   };
   auto restart = [&] {
     // the cursors restart from an opaque zero: otherwise the first steps'
-    // addresses are hoisted out of the slab loop into VGPR pairs
+    // offsets are hoisted out of the slab loop into VGPRs
     int zero;
     asm volatile("s_mov_b32 %0, 0" : "=s"(zero));
-    l_t = zero;
-    l_step = zero;
-    rows_left = rows_left0 + zero;
-    wcur = w0 + zero;
-    scur = s0 + zero;
-    bcur = b0 + zero;
+    l_ks = zero;
+    w_step = static_cast<uint32_t>(zero);
+    g_step = static_cast<uint32_t>(zero);
   };
-  ChunkStep<BITS, RPW> ring[DEPTH];
+  ChunkStep<BITS, CPL> ring[DEPTH];
   // The first slab's prologue does not depend on the routing: issue it before
   // the scan so that its latency overlaps the scan's (an expert that no pair
   // uses wastes these few loads).
@@ -632,60 +683,78 @@ __global__ __launch_bounds__(GW * kWave) void gather_kernel(GatherArgs a) {
       }
       __syncthreads();
 
-      float acc[RPW][MV], accz[RPW][MV];
+      // The slab's vector count is a compile-time constant below: the
+      // products of absent vectors vanish instead of being branched over.
+      auto slab = [&](auto nvc) {
+        constexpr int NV = decltype(nvc)::value;
+        float acc[1][MV], accz[1][MV];
 #pragma unroll
-      for (int r = 0; r < RPW; ++r)
-#pragma unroll
-        for (int m = 0; m < MV; ++m) acc[r][m] = accz[r][m] = 0.0f;
+        for (int m = 0; m < MV; ++m) acc[0][m] = accz[0][m] = 0.0f;
 
-      int c_rg = 0, c_step = 0;
-      auto consume = [&](const ChunkStep<BITS, RPW> &st) {
-        const int c = c_step * kWave + lane;
-        if (c < Kc) accumulate_chunk<BITS, RPW, MV, PAIR>(st, smem, nv, c, pk, acc, accz);
-        const bool last = c_step == nsteps - 1;
-        if (last) {                                      // row group complete
-          constexpr int V = pow2_ceil(RPW * MV);
-          float vals[V];
+        int c_rg = 0, c_ks = 0;
+        constexpr int kStride = chunk_stride<PAIR, MV>();
+        const unsigned char *xlane = smem + u * kStride;    // this lane's first staged chunk
+        auto consume = [&](const ChunkStep<BITS, CPL> &st) {
+          const int left = Kc - c_ks * KS;                 // chunks of this K range that exist
+          const unsigned char *xc = xlane + c_ks * (KS * kStride);
 #pragma unroll
-          for (int i = 0; i < V; ++i) vals[i] = 0.0f;
+          for (int i = 0; i < CPL; ++i) {
+            if (u + i * SEG < left) {
+              if constexpr (PAIR) {
+                gather_chunk_pairs<BITS, MV, NV>(st.w[i], st.s[i], st.b[i], xc + i * (SEG * kStride), pk, acc, accz);
+              } else {
+                ChunkStep<BITS, 1> one;
 #pragma unroll
-          for (int r = 0; r < RPW; ++r)
-#pragma unroll
-            for (int m = 0; m < MV; ++m) {
-              vals[r * MV + m] = PAIR ? fmaf(acc[r][m], 1.0f / static_cast<float>(1 << PairPlan<BITS>::P), accz[r][m])
-                                      : acc[r][m];
-              acc[r][m] = accz[r][m] = 0.0f;
+                for (int d = 0; d < BITS; ++d) one.w[0][d] = st.w[i][d];
+                one.s[0] = st.s[i];
+                one.b[0] = st.b[i];
+                accumulate_chunk<BITS, 1, MV, PAIR>(one, xc + i * (SEG * kStride), NV, pk, acc, accz);
+              }
             }
-          const float tot = wave_reduce_many<V>(vals, lane);
-          if (reduce_leader<V>(lane)) {
-            const int idx = reduce_index<V>(lane);
-            if (idx < RPW * MV) res[c_rg * (RPW * MV) + idx] = tot;
+          }
+          const bool last = c_ks == nks - 1;
+          if (last) {                                      // row group complete
+#pragma unroll
+            for (int m = 0; m < NV; ++m) {
+              float v = PAIR ? fmaf(acc[0][m], 1.0f / static_cast<float>(1 << PairPlan<BITS>::P), accz[0][m])
+                             : acc[0][m];
+              acc[0][m] = accz[0][m] = 0.0f;
+              // segment sum, the same lane tree for every row and vector
+              v += dpp<kDppXor1>(v);
+              v += dpp<kDppXor2>(v);
+              v += dpp<kDppHalfMirror>(v);
+              if (u == 0) res[(c_rg * R + rl) * MV + m] = v;
+            }
+          }
+          c_rg += last ? 1 : 0;
+          c_ks = last ? 0 : c_ks + 1;
+        };
+        for (int t = 0; t < T; t += DEPTH) {
+          static_for<0, DEPTH>([&](auto d) {
+            constexpr int dd = decltype(d)::value;
+            if (t + dd < T) consume(ring[dd]);
+            load_next(ring[dd]);
+          });
+        }
+
+        // ---- write out this wave's rows (its own LDS writes, in order)
+        for (int i = lane; i < RG * R * MV; i += kWave) {
+          const int g = i / (R * MV), idx = i - g * (R * MV);
+          const int r = idx / MV, mv = idx - r * MV;
+          const int64_t row = row_base + static_cast<int64_t>(g) * (GW * R) + r;
+          if (mv < NV && row < a.N) {
+            const int vec = v0 + mv;
+            const int pi = vec / a.M, m = vec - pi * a.M;
+            const int64_t o = (static_cast<int64_t>(list[pi]) * a.M + m) * a.N + row;
+            if (a.out_f32) static_cast<float *>(a.y)[o] = res[i];
+            else static_cast<uint16_t *>(a.y)[o] = f32_to_bf16(res[i]);
           }
         }
-        c_rg += last ? 1 : 0;
-        c_step = last ? 0 : c_step + 1;
       };
-      for (int t = 0; t < T; t += DEPTH) {
-        static_for<0, DEPTH>([&](auto d) {
-          constexpr int dd = decltype(d)::value;
-          if (t + dd < T) consume(ring[dd]);
-          load_next(ring[dd]);
-        });
-      }
-
-      // ---- write out this wave's rows (its own LDS writes, in order)
-      for (int i = lane; i < RG * RPW * MV; i += kWave) {
-        const int g = i / (RPW * MV), idx = i - g * (RPW * MV);
-        const int r = idx / MV, mv = idx - r * MV;
-        const int64_t row = row_base + static_cast<int64_t>(g) * (GW * RPW) + r;
-        if (mv < nv && row < a.N) {
-          const int vec = v0 + mv;
-          const int pi = vec / a.M, m = vec - pi * a.M;
-          const int64_t o = (static_cast<int64_t>(list[pi]) * a.M + m) * a.N + row;
-          if (a.out_f32) static_cast<float *>(a.y)[o] = res[i];
-          else static_cast<uint16_t *>(a.y)[o] = f32_to_bf16(res[i]);
-        }
-      }
+      if constexpr (MV >= 4) { if (nv == 4) slab(std::integral_constant<int, 4>{}); }
+      if constexpr (MV >= 3) { if (nv == 3) slab(std::integral_constant<int, 3>{}); }
+      if constexpr (MV >= 2) { if (nv == 2) slab(std::integral_constant<int, 2>{}); }
+      if (nv == 1) slab(std::integral_constant<int, 1>{});
       __syncthreads();   // LDS and list reuse by the next slab / window
     }
     if (seen <= win + kGatherListMax) return;

@@ -142,6 +142,8 @@ int qmv_silu_gate_resid(const uint16_t *gate, const uint16_t *up,
  * (every output is computed with the same arithmetic either way).
  * transpose must be 1 (else QMV_EUNSUPPORTED).  When the routed x vectors
  * average 12 or more per expert (P*M >= 12*E) the matrix cores are used.
+ * One expert's packed weight (N*K*bits/8 bytes) must be under 2 GiB (else
+ * QMV_EUNSUPPORTED): it is addressed with 32-bit offsets.
  */
 int gather_qmv(const uint16_t *x, int64_t Bx, const uint32_t *w_q,
                const uint16_t *scales, const uint16_t *biases, int64_t E,

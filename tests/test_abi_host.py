@@ -101,6 +101,10 @@ def test_gather_rejects_bad_arguments():
     # transpose=0 not implemented
     assert L.gather_qmv(*base, FAKE, FAKE, 8, *tail, 0, 0, 0, None) == \
         q.QMV_EUNSUPPORTED
+    # one expert's packed weight at 2 GiB: past the 32-bit offsets
+    assert L.gather_qmv(*base, FAKE, FAKE, 8, FAKE, 1, 1 << 20, 4096, 64, 4, 1,
+                        0, 0, None) == q.QMV_EUNSUPPORTED
+    assert "2 GiB" in L.qmv_last_error().decode()
 
 
 def test_unpack_rejects_bad_arguments():
