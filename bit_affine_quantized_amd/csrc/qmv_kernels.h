@@ -466,6 +466,27 @@ __global__ __launch_bounds__(WPB * kWave) void qmv_kernel(QmvArgs a) {
 // quad's pairs and x are live at once (instead of all 16 pairs and a whole
 // vector), and the NV chains interleave.
 // ----------------------------------------------------------------------------
+// Sum over aligned groups of SEG lanes (SEG = 8, 16, 32 or 64), by the same
+// lane tree in every group; every lane of a group receives the total.
+template <int SEG>
+__device__ __forceinline__ float segment_sum(float v) {
+  v += dpp<kDppXor1>(v);
+  v += dpp<kDppXor2>(v);
+  v += dpp<kDppHalfMirror>(v);
+  if constexpr (SEG >= 16) v += dpp<kDppRor8>(v);
+  if constexpr (SEG >= 32) {
+    float a = v, b = v;
+    swap16(a, b);
+    v = a + b;
+  }
+  if constexpr (SEG >= 64) {
+    float a = v, b = v;
+    swap32(a, b);
+    v = a + b;
+  }
+  return v;
+}
+
 template <int BITS, int MV, int NV>
 __device__ __forceinline__ void gather_chunk_pairs(const uint32_t (&w)[BITS], uint16_t sb, uint16_t bb,
                                                    const unsigned char *chunk, PairConsts pk,
@@ -541,7 +562,10 @@ struct GatherArgs {
 };
 
 constexpr int kGatherListMax = 1024;   // pairs of one expert per window
-constexpr int kGatherSeg = 8;          // lanes per row
+#ifndef QMV_GATHER_SEG
+#define QMV_GATHER_SEG 8
+#endif
+constexpr int kGatherSeg = QMV_GATHER_SEG;   // lanes per row (8, 16, 32 or 64)
 constexpr int kGatherRows = kWave / kGatherSeg;   // rows per wave step
 
 #ifndef QMV_GATHER_WPE
@@ -584,7 +608,7 @@ void gather_kernel(GatherArgs a) {
   // reading out of bounds, so the loads need no clamps or selects.  (Rows
   // past N, chunks past a row's end and steps past the wave's last are
   // loaded but never consumed.)  Every offset is in the VGPR operand, which
-  // the range check covers.  Lane (rl, u) reads chunk u of row rl of the
+  // the range check covers; the host keeps one expert under 2 GiB.  Lane (rl, u) reads chunk u of row rl of the
   // step; the scalar step offsets advance by one K range per step and to
   // the next row group (GW*R rows on) on a wrap.
   const uint32_t cb = BITS * 4;                              // bytes per chunk
@@ -601,17 +625,22 @@ void gather_kernel(GatherArgs a) {
   const uint32_t w_wrap = GW * R * wrow_b - (nks - 1) * (KS * cb);
   const uint32_t g_wrap = GW * R * grow_b - (nks - 1) * ((KS >> a.gshift) * 2);
   uint32_t w_step = 0, g_step = 0;
-  int l_ks = 0;
+  int l_t = 0, l_ks = 0;
   auto load_next = [&](ChunkStep<BITS, CPL> &st) {
+    // Steps past the wave's last are pushed out of range (2 GiB on; every
+    // lane offset is below that), so they cost no memory traffic.
+    const bool live = l_t < T;
+    const uint32_t ws = live ? w_step : 0x80000000u, gs = live ? g_step : 0x80000000u;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
-      buffer_load_chunk<BITS>(wrs, wlane + (w_step + i * SEG * cb), st.w[i]);
-      const uint32_t go = glane + (g_step + ((i * SEG) >> a.gshift) * 2);
+      buffer_load_chunk<BITS>(wrs, wlane + (ws + i * SEG * cb), st.w[i]);
+      const uint32_t go = glane + (gs + ((i * SEG) >> a.gshift) * 2);
       st.s[i] = __builtin_amdgcn_raw_buffer_load_b16(srs, go, 0, 0);
       st.b[i] = __builtin_amdgcn_raw_buffer_load_b16(brs, go, 0, 0);
     }
     // advance by selects (increments in branches end up in scratch)
     const bool wrap = l_ks + 1 == nks;
+    l_t += 1;
     l_ks = wrap ? 0 : l_ks + 1;
     w_step += wrap ? w_wrap : KS * cb;
     g_step += wrap ? g_wrap : (KS >> a.gshift) * 2;
@@ -621,6 +650,7 @@ void gather_kernel(GatherArgs a) {
     // offsets are hoisted out of the slab loop into VGPRs
     int zero;
     asm volatile("s_mov_b32 %0, 0" : "=s"(zero));
+    l_t = zero;
     l_ks = zero;
     w_step = static_cast<uint32_t>(zero);
     g_step = static_cast<uint32_t>(zero);
@@ -720,9 +750,7 @@ void gather_kernel(GatherArgs a) {
                              : acc[0][m];
               acc[0][m] = accz[0][m] = 0.0f;
               // segment sum, the same lane tree for every row and vector
-              v += dpp<kDppXor1>(v);
-              v += dpp<kDppXor2>(v);
-              v += dpp<kDppHalfMirror>(v);
+              v = segment_sum<SEG>(v);
               if (u == 0) res[(c_rg * R + rl) * MV + m] = v;
             }
           }
