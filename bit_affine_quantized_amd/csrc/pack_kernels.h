@@ -86,43 +86,76 @@ __device__ __forceinline__ uint16_t bf16_of_sum(float hi, float lo) {
   return f32_to_bf16(hi);
 }
 
-template <int BITS>
+// Each thread writes U units of 16 output bytes (8 bf16 or 4 fp32 values),
+// units t, t + T, t + 2T, ... for T threads in all, so that consecutive
+// threads write consecutive bytes and every store instruction writes one
+// contiguous run; all of a thread's loads are issued before its first
+// store.  A unit's E codes are E*b consecutive bits of its chunk (at most
+// 64, inside two consecutive words), read straight from memory: the 4 or 8
+// units of a chunk share its words through the cache.
+#ifndef QMV_DEQUANT_UNITS
+#define QMV_DEQUANT_UNITS 4
+#endif
+constexpr int kDequantUnits = QMV_DEQUANT_UNITS;
+
+template <int BITS, bool F32>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t *__restrict__ w_q,
                                                       const uint16_t *__restrict__ scales,
                                                       const uint16_t *__restrict__ biases,
-                                                      int64_t N, int64_t K, int gshift, int out_f32,
+                                                      int64_t N, int64_t K, int gshift,
                                                       void *__restrict__ out) {
+  constexpr int E = F32 ? 4 : 8;                  // values per unit
+  constexpr int U = kDequantUnits;
   const int64_t Kc = K >> 5;
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (t >= N * Kc) return;
-  const int64_t n = t / Kc, c = t - n * Kc;
-  uint32_t w[BITS];
-  load_chunk<BITS>(w_q + n * Kc * BITS + c * BITS, w);
-  const int64_t gi = n * (Kc >> gshift) + (c >> gshift);
-  const float sf = bf16_to_f32(scales[gi]);
-  const float zf = bf16_to_f32(biases[gi]);
-  float hi[32], lo[32];
-  static_for<0, 32>([&](auto k) {
-    constexpr int Kk = decltype(k)::value;
-    const float p = sf * static_cast<float>(code_at<BITS, Kk>(w));   // exact
-    const float sum = p + zf;
-    const float bb = sum - p;
-    hi[Kk] = sum;
-    lo[Kk] = (p - (sum - bb)) + (zf - bb);
-  });
-  if (out_f32) {
-    float4 *o = reinterpret_cast<float4 *>(static_cast<float *>(out) + n * K + c * 32);
+  const int64_t units = N * (K / E);
+  const int64_t T = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  uint32_t lo[U], hi[U];
+  uint16_t sb[U], bb[U];
+  int sh[U];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) o[q] = make_float4(hi[4 * q], hi[4 * q + 1], hi[4 * q + 2], hi[4 * q + 3]);
-  } else {
-    uint32_t h[16];
+  for (int i = 0; i < U; ++i) {
+    int64_t t = t0 + i * T;
+    t = t < units ? t : units - 1;                // past the end: recomputes the last unit
+    const int64_t chunk = t / (32 / E);           // flat chunk index n*Kc + c
+    const int j = static_cast<int>(t - chunk * (32 / E)) * E;   // first code of the unit
+    const int64_t n = chunk / Kc, c = chunk - n * Kc;
+    const uint32_t *cw = w_q + chunk * BITS;
+    const int bit0 = j * BITS, wi = bit0 >> 5;
+    sh[i] = bit0 & 31;
+    lo[i] = cw[wi];
+    hi[i] = (sh[i] + E * BITS > 32) ? cw[wi + 1] : 0u;   // only when the codes straddle
+    const int64_t gi = n * (Kc >> gshift) + (c >> gshift);
+    sb[i] = scales[gi];
+    bb[i] = biases[gi];
+  }
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      h[i] = static_cast<uint32_t>(bf16_of_sum(hi[2 * i], lo[2 * i])) |
-             (static_cast<uint32_t>(bf16_of_sum(hi[2 * i + 1], lo[2 * i + 1])) << 16);
-    uint4 *o = reinterpret_cast<uint4 *>(static_cast<uint16_t *>(out) + n * K + c * 32);
+  for (int i = 0; i < U; ++i) {
+    const int64_t t = t0 + i * T;
+    if (t >= units) break;
+    const uint64_t v = ((static_cast<uint64_t>(hi[i]) << 32) | lo[i]) >> sh[i];
+    const float sf = bf16_to_f32(sb[i]);
+    const float zf = bf16_to_f32(bb[i]);
+    float h[E], l[E];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) o[q] = make_uint4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]);
+    for (int e = 0; e < E; ++e) {
+      const uint32_t q = static_cast<uint32_t>(v >> (e * BITS)) & ((1u << BITS) - 1u);
+      const float p = sf * static_cast<float>(q);   // exact
+      const float sum = p + zf;
+      const float b2 = sum - p;
+      h[e] = sum;
+      l[e] = (p - (sum - b2)) + (zf - b2);
+    }
+    if constexpr (F32) {
+      reinterpret_cast<float4 *>(out)[t] = make_float4(h[0], h[1], h[2], h[3]);
+    } else {
+      uint32_t o[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        o[k] = static_cast<uint32_t>(bf16_of_sum(h[2 * k], l[2 * k])) |
+               (static_cast<uint32_t>(bf16_of_sum(h[2 * k + 1], l[2 * k + 1])) << 16);
+      reinterpret_cast<uint4 *>(out)[t] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
   }
 }
 

@@ -460,11 +460,13 @@ int run_qmm(const uint16_t *x, const uint32_t *w_q, const uint16_t *scales, cons
 template <int BITS>
 int launch_dequant_t(const uint32_t *w_q, const uint16_t *scales, const uint16_t *biases,
                      int64_t N, int64_t K, int gshift, int out_f32, void *out, hipStream_t st) {
-  const int64_t items = N * (K / 32);
-  const int64_t blocks = (items + 255) / 256;
+  const int64_t items = N * (K / (out_f32 ? 4 : 8));   // units of 16 output bytes
+  const int64_t threads = (items + qmvk::kDequantUnits - 1) / qmvk::kDequantUnits;
+  const int64_t blocks = (threads + 255) / 256;
   if (blocks > 0x7FFFFFFF) return fail(QMV_EUNSUPPORTED, "qmv_dequantize: too large");
-  hipLaunchKernelGGL(qmvk::dequant_kernel<BITS>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
-                     st, w_q, scales, biases, N, K, gshift, out_f32, out);
+  auto kern = out_f32 ? qmvk::dequant_kernel<BITS, true> : qmvk::dequant_kernel<BITS, false>;
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, w_q, scales, biases,
+                     N, K, gshift, out);
   return check_launch("qmv_dequantize");
 }
 
