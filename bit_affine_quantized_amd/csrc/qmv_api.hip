@@ -282,7 +282,13 @@ int workspace_for(hipStream_t st, size_t bytes, void **out) {
   return QMV_OK;
 }
 
-constexpr int kQvmRows = 4;   // rows in flight per stream
+#ifndef QMV_QVM_ROWS
+#define QMV_QVM_ROWS 4            // rows in flight per stream
+#endif
+#ifndef QMV_QVM_WGS
+#define QMV_QVM_WGS 1024          // split-K target: workgroups per launch
+#endif
+constexpr int kQvmRows = QMV_QVM_ROWS;
 
 template <int BITS, int MV>
 int launch_qvm_t(const qmvk::QvmArgs &a0, hipStream_t st) {
@@ -290,8 +296,10 @@ int launch_qvm_t(const qmvk::QvmArgs &a0, hipStream_t st) {
   const int64_t Nc = a.N / 32;
   const int64_t CB = (Nc + qmvk::kQvmC - 1) / qmvk::kQvmC;
   const int64_t unit = static_cast<int64_t>(kQvmRows) * qmvk::kQvmStreams;
-  // ~1024 workgroups, at most 64 slices, whole blocks of rows per slice
-  int64_t s_target = 1024 / CB;
+  // ~QMV_QVM_WGS workgroups, at most 64 slices, whole blocks of rows per
+  // slice (4096x4096 4-bit on MI355X: 4 rows per stream measured 12-15%
+  // ahead of 1 or 2, and 2048 workgroups no better than 1024)
+  int64_t s_target = QMV_QVM_WGS / CB;
   if (s_target < 1) s_target = 1;
   if (s_target > 64) s_target = 64;
   int64_t ks = (a.K + s_target - 1) / s_target;
@@ -299,7 +307,7 @@ int launch_qvm_t(const qmvk::QvmArgs &a0, hipStream_t st) {
   if (ks > 1024) ks = 1024;             // the staged x slice stays small beside the sums
   const int64_t S = (a.K + ks - 1) / ks;
   if (CB * S > 0x7FFFFFFF) return fail(QMV_EUNSUPPORTED, "qmv: transpose=0 grid too large");
-  const int64_t lds = 4 * (MV * ks + static_cast<int64_t>(qmvk::kQvmStreams) * MV * (qmvk::kQvmCols * 9 / 8));
+  const int64_t lds = 4 * (MV * ks + static_cast<int64_t>(qmvk::kQvmWaves) * MV * qmvk::kQvmRow);
   if (lds > kMaxLds) return fail(QMV_EUNSUPPORTED, "qmv: transpose=0 with K=%d too large", a.K);
   a.S = static_cast<int>(S);
   a.ks = static_cast<int>(ks);
@@ -335,13 +343,13 @@ int launch_qvm_bits(int bits, const qmvk::QvmArgs &a, hipStream_t st) {
   return fail(QMV_EINVAL, "bits=%d", bits);
 }
 
-// y = x @ W_hat with W packed [K, N] along N: slabs of up to 2 vectors.
+// y = x @ W_hat with W packed [K, N] along N: slabs of up to 4 vectors.
 int run_qvm(const uint16_t *x, const uint32_t *w_q, const uint16_t *scales, const uint16_t *biases,
             void *y, int64_t M, int64_t N, int64_t K, int group_size, int bits, int out_f32,
             hipStream_t st) {
-  for (int64_t m0 = 0; m0 < M; m0 += 2) {
+  for (int64_t m0 = 0; m0 < M; m0 += 4) {
     qmvk::QvmArgs a{};
-    const int64_t nv = M - m0 < 2 ? M - m0 : 2;
+    const int64_t nv = M - m0 < 4 ? M - m0 : 4;
     a.x = x + m0 * K;
     a.w = w_q;
     a.s = scales;
@@ -354,7 +362,9 @@ int run_qvm(const uint16_t *x, const uint32_t *w_q, const uint16_t *scales, cons
     a.M = static_cast<int>(nv);
     a.gshift = gshift_of(group_size);
     a.out_f32 = out_f32;
-    const int rc = nv == 1 ? launch_qvm_bits<1>(bits, a, st) : launch_qvm_bits<2>(bits, a, st);
+    const int rc = nv == 1 ? launch_qvm_bits<1>(bits, a, st)
+                 : nv == 2 ? launch_qvm_bits<2>(bits, a, st)
+                           : launch_qvm_bits<4>(bits, a, st);
     if (rc) return rc;
   }
   return ok();

@@ -11,10 +11,12 @@
 // A wave is C = 16 chunk lanes by 4 row streams; a workgroup (8 waves, 32
 // streams) owns a block of 16 chunks (512 columns) over one K-slice.  Each
 // stream loads its next R rows' chunks at once (all in flight), then
-// accumulates them.  The streams are summed in LDS in a fixed order.  With
-// one slice the workgroup writes y; otherwise it writes its partial block to
-// the workspace and a second kernel adds the S partials in slice order, so
-// the result does not depend on scheduling.  (A last-workgroup-finishes
+// accumulates them.  A wave first sums its 4 streams across lanes (a
+// transposing butterfly: each lane ends with 8 of its chunk's 32 columns),
+// then the 8 waves' sums meet in LDS in a fixed order.  With one slice the
+// workgroup writes y; otherwise it writes its partial block to the workspace
+// and a second kernel adds the S partials in slice order, so the result does
+// not depend on scheduling.  (A last-workgroup-finishes
 // handshake inside one kernel needs device-scope fences, which on a chip
 // with one L2 per XCD write back and invalidate L2 in every workgroup; the
 // kernel boundary pays that once.)
@@ -45,13 +47,34 @@ constexpr int kQvmWaves = 8;
 constexpr int kQvmStreams = kQvmWaves * (kWave / kQvmC);   // 32
 constexpr int kQvmCols = kQvmC * 32;         // 512 columns per block
 
+constexpr int kQvmRow = kQvmCols + kQvmCols / 8;   // 576 floats: 36 per chunk
+
+// Sum 32 values per lane over the 4 row streams of a wave (lane bits 5 and
+// 4), halving the values at each step: lane l returns the totals of values
+// 8*(l/16) .. 8*(l/16)+7 of its chunk lane l%16.
+__device__ __forceinline__ void qvm_stream_sum(const float (&v)[32], float (&out)[8]) {
+  float h[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float x = v[i], y = v[16 + i];
+    swap32(x, y);                 // lanes < 32 keep values 0..15, the others 16..31
+    h[i] = x + y;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float x = h[i], y = h[8 + i];
+    swap16(x, y);                 // even rows keep the lower 8, odd rows the upper 8
+    out[i] = x + y;
+  }
+}
+
 template <int BITS, int MV, int R>
 __global__ __launch_bounds__(kQvmWaves * kWave) void qvm_kernel(QvmArgs a) {
   constexpr int NT = kQvmWaves * kWave;
-  // x slice (fp32) then the stream partials
+  // x slice (fp32) then the per-wave sums
   extern __shared__ __align__(16) unsigned char smem[];
   float *xs = reinterpret_cast<float *>(smem);                       // [MV][ks]
-  float *red = xs + MV * a.ks;                                       // [32][MV][576]
+  float *red = xs + MV * a.ks;                                       // [8 waves][MV][576]
 
   const int64_t Nc = a.N >> 5;
   const int64_t CB = (Nc + kQvmC - 1) / kQvmC;
@@ -122,18 +145,18 @@ __global__ __launch_bounds__(kQvmWaves * kWave) void qvm_kernel(QvmArgs a) {
     }
   }
 
-  // ---- sum the 32 streams in LDS, in stream order (rows of 512 columns
-  // padded by 4 floats per 32, so a lane's 128-byte run starts on a new
-  // bank quad)
-  constexpr int kRow = kQvmCols + kQvmCols / 8;   // 576 floats
+  // ---- sum the wave's 4 streams across lanes, then the 8 waves in LDS in
+  // wave order (rows of 512 columns padded by 4 floats per 32, so a lane's
+  // 32-byte run starts on its own bank octet)
 #pragma unroll
   for (int m = 0; m < MV; ++m) {
-    float *dst = red + (stream * MV + m) * kRow + ci * 36;
+    float v[32], part[8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
-      reinterpret_cast<float4 *>(dst)[q] =
-          make_float4(acc[m][4 * q] + accz[m], acc[m][4 * q + 1] + accz[m],
-                      acc[m][4 * q + 2] + accz[m], acc[m][4 * q + 3] + accz[m]);
+    for (int i = 0; i < 32; ++i) v[i] = acc[m][i] + accz[m];
+    qvm_stream_sum(v, part);
+    float *dst = red + (wid * MV + m) * kQvmRow + ci * 36 + 8 * (lane / kQvmC);
+    reinterpret_cast<float4 *>(dst)[0] = make_float4(part[0], part[1], part[2], part[3]);
+    reinterpret_cast<float4 *>(dst)[1] = make_float4(part[4], part[5], part[6], part[7]);
   }
   __syncthreads();
   const int64_t col0 = cb * kQvmCols;
@@ -146,7 +169,7 @@ __global__ __launch_bounds__(kQvmWaves * kWave) void qvm_kernel(QvmArgs a) {
     const int m = i / kQvmCols, c = i - m * kQvmCols;
     float v = 0.0f;
 #pragma unroll
-    for (int st = 0; st < kQvmStreams; ++st) v += red[(st * MV + m) * kRow + (c >> 5) * 36 + (c & 31)];
+    for (int w = 0; w < kQvmWaves; ++w) v += red[(w * MV + m) * kQvmRow + (c >> 5) * 36 + (c & 31)];
     const int64_t n = col0 + c;
     if (a.S == 1) {
       if (m < a.M && n < a.N) store_y(m, n, v);

@@ -37,10 +37,11 @@ def _dev(w, dev):
 
 @pytest.mark.parametrize("bits", BITS)
 @pytest.mark.parametrize("g", GROUPS)
-@pytest.mark.parametrize("M", (1, 3))
+@pytest.mark.parametrize("M", (1, 3, 5))
 def test_qvm_ragged_shapes(dev, bits, g, M):
     """K = 300 rows (several split-K slices, the last one partial) and
-    N = 1152 columns (3 column blocks of 512, the last one partial)."""
+    N = 1152 columns (3 column blocks of 512, the last one partial); M = 5
+    runs as a 4-vector slab and a 1-vector slab."""
     K, N = 300, 1152
     w = _pack_kn(K, N, g, bits, seed=bits + 7 * g)
     x = synth.activation_bf16((M, K), seed=M)
