@@ -119,7 +119,7 @@ __device__ __forceinline__ void qmm_b_nibbles(uint32_t w0, uint32_t w1, const Pa
 // lane % 16).  `xoff(r, c)` is the byte offset from `x` of chunk c of staged
 // row r (r < 16*BM, callers clamp it to a valid row).  Every thread of the
 // workgroup must call this (it holds workgroup barriers).
-template <int BITS, int BM, int CPG, typename XOff>
+template <int BITS, int BM, int CPG, int GW, typename XOff>
 __device__ __forceinline__ void qmm_accumulate(const uint32_t *__restrict__ w, const uint16_t *__restrict__ sp,
                                                const uint16_t *__restrict__ bp_, const uint16_t *__restrict__ x,
                                                uint32_t nrow, int Kc, int c0, int c1, XOff &&xoff,
@@ -154,9 +154,22 @@ __device__ __forceinline__ void qmm_accumulate(const uint32_t *__restrict__ w, c
     Dh[t] = acc[t];
   }
 
+  constexpr int kThreads = GW * kWave;
+  constexpr int kItems = (MR * kQmmKB + kThreads - 1) / kThreads;   // x chunks per thread
   for (int cb = c0; cb < c1; cb += kQmmKB) {
-    // this block's weight windows, scales and biases first: their latency
-    // overlaps the staging (chunks past the range re-read its last chunk).
+    // ---- this block's x chunks (rows [0, MR) x chunks [cb, cb + KB)) are
+    // loaded first, then the weight windows, scales and biases: the memory
+    // counter retires loads in order, so converting x waits for x alone and
+    // the weights' latency overlaps the conversion.  Chunks past the range
+    // restage a valid chunk (their products are never used); items past
+    // the block's count reload its last item and are dropped.
+    uint32_t raw[kItems][16];
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+      const int it = min(static_cast<int>(threadIdx.x) + i * kThreads, MR * kQmmKB - 1);
+      const int cc = it / MR, r = it - cc * MR;
+      load_x_chunk(byte_offset(x, xoff(r, min(cb + cc, c1 - 1))), raw[i]);
+    }
     // Plain loads, not non-temporal ones: a lane's window is a few bytes of
     // a row, and the block's chunks read the rest of the same cache lines,
     // which non-temporal loads would not keep (measured 13% slower at
@@ -177,31 +190,31 @@ __device__ __forceinline__ void qmm_accumulate(const uint32_t *__restrict__ w, c
       za[gg] = *byte_offset(bp_, (nrow * gpr + gi) * 2u);
     }
     __syncthreads();                              // the previous block's LDS reads are done
-    // ---- stage x rows [0, MR) x chunks [cb, cb + KB) in pair order.  Chunks
-    // past the range restage a valid chunk: their products are never used.
-    // Consecutive threads take consecutive rows of one chunk: their 16-byte
-    // LDS stores are 80 bytes apart (no bank conflicts), as are the sums.
-    for (int it = threadIdx.x; it < MR * kQmmKB; it += kQmmThreads) {
-      const int cc = it / MR, r = it - cc * MR;
-      const int c = min(cb + cc, c1 - 1);
-      uint32_t raw[16];
-      load_x_chunk(byte_offset(x, xoff(r, c)), raw);
-      float sum = 0.0f;
+    // ---- convert to pair order into LDS.  Consecutive threads take
+    // consecutive rows of one chunk: their 16-byte LDS stores are 80 bytes
+    // apart (no bank conflicts), as are the sums.
 #pragma unroll
-      for (int q = 0; q < 16; ++q) sum = dot2_bf16(raw[q], 0x3F803F80u, sum);
-      unsigned char *dst = xp + (cc * MR + r) * kQmmRow;
+    for (int i = 0; i < kItems; ++i) {
+      const int it = static_cast<int>(threadIdx.x) + i * kThreads;
+      if (it < MR * kQmmKB) {
+        const int cc = it / MR, r = it - cc * MR;
+        float sum = 0.0f;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint32_t pr[4];
+        for (int q = 0; q < 16; ++q) sum = dot2_bf16(raw[i][q], 0x3F803F80u, sum);
+        unsigned char *dst = xp + (cc * MR + r) * kQmmRow;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          // pair 4q + e = (x[8q + e], x[8q + e + 4])
-          pr[e] = __builtin_amdgcn_perm(raw[4 * q + 2 + (e >> 1)], raw[4 * q + (e >> 1)],
-                                        (e & 1) ? 0x07060302u : 0x05040100u);
+        for (int q = 0; q < 4; ++q) {
+          uint32_t pr[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            // pair 4q + e = (x[8q + e], x[8q + e + 4])
+            pr[e] = __builtin_amdgcn_perm(raw[i][4 * q + 2 + (e >> 1)], raw[i][4 * q + (e >> 1)],
+                                          (e & 1) ? 0x07060302u : 0x05040100u);
+          }
+          *reinterpret_cast<uint4 *>(dst + q * 16) = make_uint4(pr[0], pr[1], pr[2], pr[3]);
         }
-        *reinterpret_cast<uint4 *>(dst + q * 16) = make_uint4(pr[0], pr[1], pr[2], pr[3]);
+        xsum[cc * MR + r] = sum;
       }
-      xsum[cc * MR + r] = sum;
     }
     __syncthreads();
 
@@ -268,7 +281,7 @@ __global__ __launch_bounds__(kQmmThreads) void qmm_kernel(QmmArgs a) {
   // rows past M restage row M - 1: their outputs are never stored
   auto xoff = [&](int r, int c) { return static_cast<uint32_t>(min(r, a.M - 1) * a.K + c * 32) * 2u; };
   f32x4_t acc[BM], accz[BM];
-  qmm_accumulate<BITS, BM, CPG>(a.w, a.s, a.b, a.x, nrow, Kc, c0, c1, xoff, smem, acc, accz);
+  qmm_accumulate<BITS, BM, CPG, kQmmWaves>(a.w, a.s, a.b, a.x, nrow, Kc, c0, c1, xoff, smem, acc, accz);
 
   // ---- lane holds rows 4*kb + e of each m-tile, column n
   constexpr float kInvP = 1.0f / static_cast<float>(1 << P);
@@ -316,24 +329,34 @@ struct GatherQmmArgs {
 };
 
 constexpr int kGqmmListMax = 1024;
+// Waves per gathered workgroup (16 W rows each): twice the plain product's,
+// so each staged block of routed x serves 128 W rows (512 tokens x top-8
+// over 64 experts of 2048x2048 on MI355X: 311 -> 280 us; the plain product
+// measured 4-7% slower with 8).
+#ifndef QMV_GQMM_WAVES
+#define QMV_GQMM_WAVES 8
+#endif
+constexpr int kGqmmWaves = QMV_GQMM_WAVES;
+constexpr int kGqmmThreads = kGqmmWaves * kWave;
+constexpr int kGqmmRowsPerWG = 16 * kGqmmWaves;
 
 template <int BITS, int CPG>
-__global__ __launch_bounds__(kQmmThreads) void gather_qmm_kernel(GatherQmmArgs a) {
+__global__ __launch_bounds__(kGqmmThreads) void gather_qmm_kernel(GatherQmmArgs a) {
   constexpr int BM = 4, MR = 64;
   constexpr int P = BITS == 8 ? 3 : 7 - BITS;
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int list[kGqmmListMax];
   __shared__ int xrow[kGqmmListMax];
   __shared__ uint32_t rowoff[MR];                  // x byte offset of each staged row
-  __shared__ int wcnt[kQmmWaves];
+  __shared__ int wcnt[kGqmmWaves];
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int kb = lane >> 4;
-  const int64_t NB = (a.N + kQmmRowsPerWG - 1) / kQmmRowsPerWG;
+  const int64_t NB = (a.N + kGqmmRowsPerWG - 1) / kGqmmRowsPerWG;
   const int e = static_cast<int>(blockIdx.x / NB);
   const int64_t nb = blockIdx.x % NB;
-  const int64_t n = nb * kQmmRowsPerWG + wid * 16 + (lane & 15);
+  const int64_t n = nb * kGqmmRowsPerWG + wid * 16 + (lane & 15);
   const uint32_t nrow = static_cast<uint32_t>(n < a.N ? n : a.N - 1);
   const int Kc = a.K >> 5;
   const int64_t wrows = static_cast<int64_t>(e) * a.N;
@@ -348,7 +371,7 @@ __global__ __launch_bounds__(kQmmThreads) void gather_qmm_kernel(GatherQmmArgs a
     // counts gives its first rank: ranks follow p whatever the order of rhs.
     constexpr int kRun = 16;
     int seen = 0;
-    for (int64_t base = 0; base < a.P; base += static_cast<int64_t>(kQmmThreads) * kRun) {
+    for (int64_t base = 0; base < a.P; base += static_cast<int64_t>(kGqmmThreads) * kRun) {
       const int64_t p0 = base + static_cast<int64_t>(threadIdx.x) * kRun;
       uint32_t hits = 0;
 #pragma unroll
@@ -369,7 +392,7 @@ __global__ __launch_bounds__(kQmmThreads) void gather_qmm_kernel(GatherQmmArgs a
       int before = seen + incl - cnt;
       int round = 0;
 #pragma unroll
-      for (int w = 0; w < kQmmWaves; ++w) {
+      for (int w = 0; w < kGqmmWaves; ++w) {
         const int c = wcnt[w];
         before += (w < wid) ? c : 0;
         round += c;
@@ -401,7 +424,7 @@ __global__ __launch_bounds__(kQmmThreads) void gather_qmm_kernel(GatherQmmArgs a
       __syncthreads();
       auto xoff = [&](int r, int c) { return rowoff[r] + static_cast<uint32_t>(c) * 64u; };
       f32x4_t acc[BM], accz[BM];
-      qmm_accumulate<BITS, BM, CPG>(we, se, be, a.x, nrow, Kc, 0, Kc, xoff, smem, acc, accz);
+      qmm_accumulate<BITS, BM, CPG, kGqmmWaves>(we, se, be, a.x, nrow, Kc, 0, Kc, xoff, smem, acc, accz);
 
       constexpr float kInvP = 1.0f / static_cast<float>(1 << P);
 #pragma unroll

@@ -220,12 +220,12 @@ int launch_gather_t(const qmvk::GatherArgs &a0, int64_t E, hipStream_t st) {
 
 template <int BITS, int CPG>
 int launch_gather_qmm_t(const qmvk::GatherQmmArgs &a, int64_t E, hipStream_t st) {
-  const int64_t NB = (a.N + qmvk::kQmmRowsPerWG - 1) / qmvk::kQmmRowsPerWG;
+  const int64_t NB = (a.N + qmvk::kGqmmRowsPerWG - 1) / qmvk::kGqmmRowsPerWG;
   if (E * NB > 0x7FFFFFFF) return fail(QMV_EUNSUPPORTED, "gather_qmv: grid too large");
   constexpr int lds = qmvk::qmm_lds_bytes<4>();
   auto kern = qmvk::gather_qmm_kernel<BITS, CPG>;
   allow_lds(kern, lds);
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(E * NB)), dim3(qmvk::kQmmThreads), lds, st, a);
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(E * NB)), dim3(qmvk::kGqmmThreads), lds, st, a);
   return check_launch("gather_qmv (matrix cores)");
 }
 
