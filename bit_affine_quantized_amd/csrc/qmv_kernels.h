@@ -125,6 +125,11 @@ __device__ __forceinline__ void stage_f32_chunk(const uint16_t *__restrict__ xk,
 }
 
 // h = silu(gate) * up in fp32 (metrale QuantWeights::gemv_silu_gate_resid).
+// The quotient g / (1 + e^-g) is taken as g times the hardware reciprocal
+// (v_rcp_f32, within 1 ulp) instead of an IEEE division: every workgroup
+// recomputes h for the whole K, and the division's scale/refine/fixup
+// sequence was most of that cost.  h then carries a few ulp of fp32 error,
+// far inside the fp32 output tolerance.
 __device__ __forceinline__ void stage_silu_raw(const uint32_t (&graw)[16], const uint32_t (&uraw)[16],
                                                unsigned char *lds, int c) {
   float v[32];
@@ -132,7 +137,7 @@ __device__ __forceinline__ void stage_silu_raw(const uint32_t (&graw)[16], const
   for (int k = 0; k < 32; ++k) {
     const float g = raw_x(graw, k);
     const float u = raw_x(uraw, k);
-    v[k] = g / (1.0f + __expf(-g)) * u;
+    v[k] = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
   }
   store_f32_chunk<1>(v, lds, 0, c);
 }
