@@ -325,6 +325,23 @@ def test_gather_small(dev, bits, M):
         _run_gather(dev, x, ew, lhs[perm], rhs[perm], g, bits, True), y[perm])
 
 
+@pytest.mark.parametrize("E,N,K,g,bits", [(3, 1, 64, 64, 4), (5, 7, 96, 32, 3),
+                                          (4, 9, 2112, 64, 8), (2, 33, 320, 64, 6)])
+def test_gather_row_and_k_edges(dev, E, N, K, g, bits):
+    """Row counts below and just past one 8-row wave step (N = 1, 7, 9, 33)
+    and K ranges that leave most lanes of a row segment idle (2 or 3
+    chunks) or end one chunk into a step (66 and 10 chunks)."""
+    ew = _experts(E, N, K, bits, g, seed0=300 + N)
+    rng = np.random.default_rng(N + K)
+    Bx, P = 3, 11
+    x = synth.activation_bf16((Bx, 1, K), seed=N)
+    lhs = rng.integers(0, Bx, P).astype(np.uint32)
+    rhs = rng.integers(0, E, P).astype(np.uint32)
+    ref = oracle.gather_qmv(x, *ew, lhs, rhs, g, bits)
+    check_t1(_run_gather(dev, x, ew, lhs, rhs, g, bits, False), ref)
+    check_t2(_run_gather(dev, x, ew, lhs, rhs, g, bits, False, True), ref)
+
+
 @pytest.mark.parametrize("sorted_indices", (False, True))
 def test_gather_long_pair_lists(dev, sorted_indices):
     """2500 pairs over 300 experts (8.3 per expert on average: the matvec
