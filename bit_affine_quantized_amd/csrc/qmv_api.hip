@@ -100,13 +100,20 @@ constexpr int kRpw = QMV_RPW;
 #define QMV_FORCE_WPB 0   // 4 or 8 forces the waves per workgroup; 0 chooses by LDS
 #endif
 
-template <int BITS, int MV, int XIN, int WPB>
+#ifndef QMV_SMALL_ROWS
+// At most this many rows: one row per wave in 8-wave workgroups, so that a
+// small matrix still fills the wave slots (4096x4096 4-bit on MI355X, one
+// vector: 4.46 -> 4.20 us; at 14336 rows two rows per wave stay faster).
+#define QMV_SMALL_ROWS 4096
+#endif
+
+template <int BITS, int MV, int XIN, int WPB, int RPW = kRpw>
 int launch_qmv_wpb(const qmvk::QmvArgs &a, int64_t lds, hipStream_t st) {
   const int64_t rows = static_cast<int64_t>(a.nmat) * a.N;
-  const int64_t rows_per_block = WPB * kRpw;
+  const int64_t rows_per_block = WPB * RPW;
   const int64_t blocks = (rows + rows_per_block - 1) / rows_per_block;
   if (blocks > 0x7FFFFFFF) return fail(QMV_EUNSUPPORTED, "qmv: too many rows");
-  auto kern = qmvk::qmv_kernel<BITS, kRpw, MV, XIN, WPB>;
+  auto kern = qmvk::qmv_kernel<BITS, RPW, MV, XIN, WPB>;
   allow_lds(kern, lds);
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(WPB * qmvk::kWave),
                      static_cast<size_t>(lds), st, a);
@@ -129,6 +136,10 @@ int launch_qmv_t(const qmvk::QmvArgs &a, hipStream_t st) {
   constexpr bool PAIR = (BITS <= 6) && (XIN == qmvk::XIN_PLAIN);
   const int64_t Kc = a.K / 32;
   const int64_t lds = Kc * qmvk::chunk_stride<PAIR, (XIN == qmvk::XIN_SILU ? 1 : MV)>();
+  if constexpr (XIN == qmvk::XIN_PLAIN) {
+    if (static_cast<int64_t>(a.nmat) * a.N <= QMV_SMALL_ROWS && !QMV_FORCE_WPB)
+      return launch_qmv_wpb<BITS, MV, XIN, 8, 1>(a, lds, st);
+  }
   if (qmv_waves_per_block(lds) == 4) return launch_qmv_wpb<BITS, MV, XIN, 4>(a, lds, st);
   return launch_qmv_wpb<BITS, MV, XIN, 8>(a, lds, st);
 }
