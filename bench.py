@@ -41,7 +41,8 @@ METRIC = "qmv GB/s & % of HBM peak, 4-bit g64 N=14336 K=4096 batch 1"
 HBM_PEAK_GBS = 8000.0
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [os.path.join(ROOT, "bit_affine_quantized_amd", "csrc", f)
-                  for f in ("qmv_device.h", "qmv_kernels.h", "qmv_api.hip")]
+                  for f in ("qmv_device.h", "qmv_kernels.h", "qmv_api.hip", "pack_kernels.h",
+                            "qvm_kernels.h", "qmm_kernels.h")]
 ROTATE_BYTES = 512e6
 
 

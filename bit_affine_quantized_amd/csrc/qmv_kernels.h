@@ -537,16 +537,16 @@ __device__ __forceinline__ void gather_chunk_pairs(const uint32_t (&w)[BITS], ui
 // so sorted and unsorted indices run identical arithmetic for every output.
 // Lists longer than kGatherListMax are processed in windows.
 //
-// Rows are cut into segments of 8 lanes: a wave step covers 8 rows, and lane
-// u of a row's segment takes chunks u, u + 8, ..., u + 8 (CPL - 1) of the
-// step's K range, so each of the CPL loads reads 8 x (chunk bytes) contiguous
-// bytes of every row.  A row's partial sums meet in a 3-level DPP reduction
-// inside its segment once per row group, not once per step: with few x
-// vectors per expert the per-row reduction and bookkeeping of a
-// one-row-per-wave layout cost as much as the dot products.  Each wave
-// streams its row groups (tile_rows / (waves x 8) of them, each K / (8 x 32
-// CPL) steps long) through a DEPTH-deep load ring; loads are branch-free
-// (clamped).
+// Rows are cut into segments of SEG lanes (8 by default): a wave step covers
+// 64 / SEG rows, and lane u of a row's segment takes chunks u, u + SEG, ...,
+// u + SEG (CPL - 1) of the step's K range, so each of the CPL loads reads
+// SEG x (chunk bytes) contiguous bytes of every row.  A row's partial sums
+// meet in a DPP reduction inside its segment once per row group, not once
+// per step: with few x vectors per expert the per-row reduction and
+// bookkeeping of a one-row-per-wave layout cost as much as the dot products.
+// Each wave streams its row groups (tile_rows / (waves x rows per step) of
+// them, each K / (SEG x 32 CPL) steps long) through a DEPTH-deep load ring
+// of branch-free buffer loads.
 // ----------------------------------------------------------------------------
 struct GatherArgs {
   const uint16_t *x;        // [Bx, M, K]
@@ -573,12 +573,8 @@ constexpr int kGatherListMax = 1024;   // pairs of one expert per window
 constexpr int kGatherSeg = QMV_GATHER_SEG;   // lanes per row (8, 16, 32 or 64)
 constexpr int kGatherRows = kWave / kGatherSeg;   // rows per wave step
 
-#ifndef QMV_GATHER_WPE
-#define QMV_GATHER_WPE 1
-#endif
 template <int BITS, int MV, int GW, int DEPTH, int CPL>
-__global__ __launch_bounds__(GW * kWave) __attribute__((amdgpu_waves_per_eu(QMV_GATHER_WPE)))
-void gather_kernel(GatherArgs a) {
+__global__ __launch_bounds__(GW * kWave) void gather_kernel(GatherArgs a) {
   constexpr bool PAIR = BITS <= 6;
   constexpr int NT = GW * kWave;
   constexpr int SEG = kGatherSeg, R = kGatherRows, KS = SEG * CPL;
