@@ -325,6 +325,8 @@ struct GatherQmmArgs {
   int K;
   int M;
   int out_f32;
+  int slabs;                // workgroups per (expert, row block): slab s takes
+                            // x vectors [64 s, 64 s + 64), [64 (s + slabs), ...), ...
   void *y;                  // [P, M, N]
 };
 
@@ -354,8 +356,12 @@ __global__ __launch_bounds__(kGqmmThreads) void gather_qmm_kernel(GatherQmmArgs 
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int kb = lane >> 4;
   const int64_t NB = (a.N + kGqmmRowsPerWG - 1) / kGqmmRowsPerWG;
-  const int e = static_cast<int>(blockIdx.x / NB);
-  const int64_t nb = blockIdx.x % NB;
+  // slab index outermost: every expert's first slab is dispatched first
+  const int64_t per_slab = gridDim.x / a.slabs;
+  const int sidx = static_cast<int>(blockIdx.x / per_slab);
+  const int64_t rest = blockIdx.x - sidx * per_slab;
+  const int e = static_cast<int>(rest / NB);
+  const int64_t nb = rest % NB;
   const int64_t n = nb * kGqmmRowsPerWG + wid * 16 + (lane & 15);
   const uint32_t nrow = static_cast<uint32_t>(n < a.N ? n : a.N - 1);
   const int Kc = a.K >> 5;
@@ -414,7 +420,7 @@ __global__ __launch_bounds__(kGqmmThreads) void gather_qmm_kernel(GatherQmmArgs 
     if (npairs <= 0) return;                       // uniform
     const int nvec = npairs * a.M;
 
-    for (int v0 = 0; v0 < nvec; v0 += MR) {
+    for (int v0 = sidx * MR; v0 < nvec; v0 += MR * a.slabs) {
       const int nv = min(MR, nvec - v0);
       if (threadIdx.x < MR) {
         const int vec = v0 + min(static_cast<int>(threadIdx.x), nv - 1);   // past nv: restage the last

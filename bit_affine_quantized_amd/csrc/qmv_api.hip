@@ -230,13 +230,25 @@ int launch_gather_t(const qmvk::GatherArgs &a0, int64_t E, hipStream_t st) {
 #endif
 
 template <int BITS, int CPG>
-int launch_gather_qmm_t(const qmvk::GatherQmmArgs &a, int64_t E, hipStream_t st) {
+int launch_gather_qmm_t(const qmvk::GatherQmmArgs &a0, int64_t E, hipStream_t st) {
+  qmvk::GatherQmmArgs a = a0;
   const int64_t NB = (a.N + qmvk::kGqmmRowsPerWG - 1) / qmvk::kGqmmRowsPerWG;
-  if (E * NB > 0x7FFFFFFF) return fail(QMV_EUNSUPPORTED, "gather_qmv: grid too large");
+  // Slabs of 64 x vectors run in parallel workgroups: an expert routed more
+  // than 64 vectors would otherwise take its slabs one after another and set
+  // the kernel's critical path.  1.5x the mean slab count per expert covers
+  // the usual spread; an expert with more slabs loops over them.  (512 tokens
+  // x top-8 over 64 experts on MI355X, ~64 vectors per expert.)
+  const int64_t mean_vec = (a.P * a.M + E - 1) / E;
+  int64_t slabs = (3 * mean_vec + 127) / 128;
+  if (slabs < 1) slabs = 1;
+  if (slabs > 8) slabs = 8;
+  if (slabs * E * NB > 0x7FFFFFFF) return fail(QMV_EUNSUPPORTED, "gather_qmv: grid too large");
+  a.slabs = static_cast<int>(slabs);
   constexpr int lds = qmvk::qmm_lds_bytes<4>();
   auto kern = qmvk::gather_qmm_kernel<BITS, CPG>;
   allow_lds(kern, lds);
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(E * NB)), dim3(qmvk::kGqmmThreads), lds, st, a);
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(slabs * E * NB)), dim3(qmvk::kGqmmThreads), lds,
+                     st, a);
   return check_launch("gather_qmv (matrix cores)");
 }
 
