@@ -61,7 +61,7 @@ constexpr int kQmmRowsPerWG = 16 * kQmmWaves;    // W rows per workgroup
 
 template <int BM>
 constexpr int qmm_lds_bytes() {
-  return kQmmKB * 16 * BM * kQmmRow + kQmmKB * 16 * BM * 4;
+  return kQmmKB * 16 * BM * kQmmRow + kQmmKB * 16 * BM * 4;   // pairs + (at most per-chunk) sums
 }
 
 // Magic-bf16 B operand (4 dwords = 8 bf16) from the lane's window: pair j
@@ -129,7 +129,7 @@ __device__ __forceinline__ void qmm_accumulate(const uint32_t *__restrict__ w, c
   constexpr float kZc = NIB ? 272.0f : static_cast<float>(1 << BITS);   // z - kZc * s
   constexpr int GPB = kQmmKB / CPG;               // groups per K-block
   unsigned char *xp = smem;                                       // [KB][MR][80]
-  float *xsum = reinterpret_cast<float *>(smem + kQmmKB * MR * kQmmRow);   // [KB][MR]
+  float *xsum = reinterpret_cast<float *>(smem + kQmmKB * MR * kQmmRow);   // [GPB][MR] group sums
   const int lane = threadIdx.x & (kWave - 1);
   const int j = lane & 15, kb = lane >> 4;
   const uint32_t gpr = static_cast<uint32_t>(Kc / CPG);           // groups per row
@@ -155,7 +155,11 @@ __device__ __forceinline__ void qmm_accumulate(const uint32_t *__restrict__ w, c
   }
 
   constexpr int kThreads = GW * kWave;
-  constexpr int kItems = (MR * kQmmKB + kThreads - 1) / kThreads;   // x chunks per thread
+  // A staging item is one chunk of one row.  The CPG chunks of a row's group
+  // sit in adjacent lanes (item = (group, row, chunk), chunk fastest), so
+  // the group's x sum is their chunk sums added across lanes, formed once.
+  constexpr int kUnits = MR * kQmmKB;
+  constexpr int kItems = (kUnits + kThreads - 1) / kThreads;   // items per thread
   for (int cb = c0; cb < c1; cb += kQmmKB) {
     // ---- this block's x chunks (rows [0, MR) x chunks [cb, cb + KB)) are
     // loaded first, then the weight windows, scales and biases: the memory
@@ -166,9 +170,10 @@ __device__ __forceinline__ void qmm_accumulate(const uint32_t *__restrict__ w, c
     uint32_t raw[kItems][16];
 #pragma unroll
     for (int i = 0; i < kItems; ++i) {
-      const int it = min(static_cast<int>(threadIdx.x) + i * kThreads, MR * kQmmKB - 1);
-      const int cc = it / MR, r = it - cc * MR;
-      load_x_chunk(byte_offset(x, xoff(r, min(cb + cc, c1 - 1))), raw[i]);
+      const int it = min(static_cast<int>(threadIdx.x) + i * kThreads, kUnits - 1);
+      const int ch = it % CPG, rest = it / CPG;
+      const int r = rest % MR, gg = rest / MR;
+      load_x_chunk(byte_offset(x, xoff(r, min(cb + gg * CPG + ch, c1 - 1))), raw[i]);
     }
     // Plain loads, not non-temporal ones: a lane's window is a few bytes of
     // a row, and the block's chunks read the rest of the same cache lines,
@@ -190,18 +195,22 @@ __device__ __forceinline__ void qmm_accumulate(const uint32_t *__restrict__ w, c
       za[gg] = *byte_offset(bp_, (nrow * gpr + gi) * 2u);
     }
     __syncthreads();                              // the previous block's LDS reads are done
-    // ---- convert to pair order into LDS.  Consecutive threads take
-    // consecutive rows of one chunk: their 16-byte LDS stores are 80 bytes
-    // apart (no bank conflicts), as are the sums.
+    // ---- convert to pair order into LDS.  Rows of one chunk are 80 bytes
+    // apart, so a chunk's 16-byte stores do not collide on banks.
 #pragma unroll
     for (int i = 0; i < kItems; ++i) {
-      const int it = static_cast<int>(threadIdx.x) + i * kThreads;
-      if (it < MR * kQmmKB) {
-        const int cc = it / MR, r = it - cc * MR;
-        float sum = 0.0f;
+      const int it_raw = static_cast<int>(threadIdx.x) + i * kThreads;
+      const int it = min(it_raw, kUnits - 1);
+      const int ch = it % CPG, rest = it / CPG;
+      const int r = rest % MR, gg = rest / MR;
+      float sum = 0.0f;
 #pragma unroll
-        for (int q = 0; q < 16; ++q) sum = dot2_bf16(raw[i][q], 0x3F803F80u, sum);
-        unsigned char *dst = xp + (cc * MR + r) * kQmmRow;
+      for (int q = 0; q < 16; ++q) sum = dot2_bf16(raw[i][q], 0x3F803F80u, sum);
+      // the group's sum: chunk sums of adjacent lanes, lower chunk first
+      if constexpr (CPG >= 2) sum += dpp<kDppXor1>(sum);
+      if constexpr (CPG >= 4) sum += dpp<kDppXor2>(sum);
+      if (it_raw < kUnits) {
+        unsigned char *dst = xp + ((gg * CPG + ch) * MR + r) * kQmmRow;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           uint32_t pr[4];
@@ -213,7 +222,7 @@ __device__ __forceinline__ void qmm_accumulate(const uint32_t *__restrict__ w, c
           }
           *reinterpret_cast<uint4 *>(dst + q * 16) = make_uint4(pr[0], pr[1], pr[2], pr[3]);
         }
-        xsum[cc * MR + r] = sum;
+        if (ch == 0) xsum[gg * MR + r] = sum;
       }
     }
     __syncthreads();
@@ -242,12 +251,7 @@ __device__ __forceinline__ void qmm_accumulate(const uint32_t *__restrict__ w, c
           const float zc = fmaf(-kZc, s, bf16_to_f32(za[cc / CPG]));
 #pragma unroll
           for (int t = 0; t < BM; ++t) {
-            float4 xg = *reinterpret_cast<const float4 *>(xsum + (cc - CPG + 1) * MR + t * 16 + 4 * kb);
-#pragma unroll
-            for (int q = 1; q < CPG; ++q) {
-              const float4 v = *reinterpret_cast<const float4 *>(xsum + (cc - CPG + 1 + q) * MR + t * 16 + 4 * kb);
-              xg.x += v.x; xg.y += v.y; xg.z += v.z; xg.w += v.w;
-            }
+            const float4 xg = *reinterpret_cast<const float4 *>(xsum + (cc / CPG) * MR + t * 16 + 4 * kb);
             const float xgv[4] = {xg.x, xg.y, xg.z, xg.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
