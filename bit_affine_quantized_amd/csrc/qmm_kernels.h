@@ -155,32 +155,38 @@ __device__ __forceinline__ void qmm_accumulate(const uint32_t *__restrict__ w, c
   }
 
   constexpr int kThreads = GW * kWave;
-  // A staging item is one chunk of one row.  The CPG chunks of a row's group
-  // sit in adjacent lanes (item = (group, row, chunk), chunk fastest), so
-  // the group's x sum is their chunk sums added across lanes, formed once.
-  constexpr int kUnits = MR * kQmmKB;
-  constexpr int kItems = (kUnits + kThreads - 1) / kThreads;   // items per thread
   for (int cb = c0; cb < c1; cb += kQmmKB) {
     // ---- this block's x chunks (rows [0, MR) x chunks [cb, cb + KB)) are
     // loaded first, then the weight windows, scales and biases: the memory
     // counter retires loads in order, so converting x waits for x alone and
     // the weights' latency overlaps the conversion.  Chunks past the range
-    // restage a valid chunk (their products are never used); items past
-    // the block's count reload its last item and are dropped.
-    uint32_t raw[kItems][16];
+    // restage a valid chunk (their products are never used).
+    //
+    // Each 64-byte chunk of a row is loaded by four adjacent lanes, 16 bytes
+    // (one lane group's 8 codes) each, so that one load instruction covers
+    // whole cache lines: piece p = (group, row, chunk, quarter), quarter
+    // fastest.  The CPG chunks of a row's group then sit in adjacent quads,
+    // and the group's x sum is formed across those lanes, once.  (Whole
+    // chunks per lane read 32 bytes of a line per request: 193 -> 175 us on
+    // the 512-token top-8 gather over 64 experts.)
+    constexpr int kPieces = MR * kQmmKB * 4;
+    static_assert(kPieces % kThreads == 0, "x pieces must divide evenly");
+    constexpr int kPer = kPieces / kThreads;
+    uint4 raw[kPer];
 #pragma unroll
-    for (int i = 0; i < kItems; ++i) {
-      const int it = min(static_cast<int>(threadIdx.x) + i * kThreads, kUnits - 1);
+    for (int i = 0; i < kPer; ++i) {
+      const int pc = static_cast<int>(threadIdx.x) + i * kThreads;
+      const int qq = pc & 3, it = pc >> 2;
       const int ch = it % CPG, rest = it / CPG;
       const int r = rest % MR, gg = rest / MR;
-      load_x_chunk(byte_offset(x, xoff(r, min(cb + gg * CPG + ch, c1 - 1))), raw[i]);
+      raw[i] = *reinterpret_cast<const uint4 *>(
+          byte_offset(x, xoff(r, min(cb + gg * CPG + ch, c1 - 1)) + static_cast<uint32_t>(qq * 16)));
     }
     // Plain loads, not non-temporal ones: a lane's window is a few bytes of
     // a row, and the block's chunks read the rest of the same cache lines,
     // which non-temporal loads would not keep (measured 13% slower at
     // 4096x4096, M = 16).
     uint32_t wa[kQmmKB], wb[kQmmKB];
-    uint16_t sa[GPB], za[GPB];
 #pragma unroll
     for (int cc = 0; cc < kQmmKB; ++cc) {
       const uint32_t c = static_cast<uint32_t>(min(cb + cc, c1 - 1));
@@ -188,42 +194,49 @@ __device__ __forceinline__ void qmm_accumulate(const uint32_t *__restrict__ w, c
       wa[cc] = *byte_offset(w, off);
       wb[cc] = *byte_offset(w, off + w_second);
     }
+    // Scales and biases: lane group kb loads those of the block's groups kb
+    // and kb + 4 for its row, packed (scale low, bias high); the fold takes
+    // group gg's from lane j + 16 (gg % 4).  One load instruction then
+    // serves four groups of the 16 rows instead of one: each of these 2-byte
+    // loads costs a cache-line request per row, and the requests, not the
+    // bytes, set the pace (4096x4096, M = 16: 14.6 -> 12.1 us; the 512-token
+    // top-8 gather over 64 experts: 254 -> 193 us).
+    constexpr int kSzLoads = (GPB + 3) / 4;
+    uint32_t sz[kSzLoads];
 #pragma unroll
-    for (int gg = 0; gg < GPB; ++gg) {
+    for (int q = 0; q < kSzLoads; ++q) {
+      const int gg = min(kb + 4 * q, GPB - 1);
       const uint32_t gi = static_cast<uint32_t>(min(cb + gg * CPG, c1 - 1)) / CPG;
-      sa[gg] = *byte_offset(sp, (nrow * gpr + gi) * 2u);
-      za[gg] = *byte_offset(bp_, (nrow * gpr + gi) * 2u);
+      const uint32_t o = (nrow * gpr + gi) * 2u;
+      sz[q] = static_cast<uint32_t>(*byte_offset(sp, o)) | (static_cast<uint32_t>(*byte_offset(bp_, o)) << 16);
     }
     __syncthreads();                              // the previous block's LDS reads are done
     // ---- convert to pair order into LDS.  Rows of one chunk are 80 bytes
     // apart, so a chunk's 16-byte stores do not collide on banks.
 #pragma unroll
-    for (int i = 0; i < kItems; ++i) {
-      const int it_raw = static_cast<int>(threadIdx.x) + i * kThreads;
-      const int it = min(it_raw, kUnits - 1);
+    for (int i = 0; i < kPer; ++i) {
+      const int pc = static_cast<int>(threadIdx.x) + i * kThreads;
+      const int qq = pc & 3, it = pc >> 2;
       const int ch = it % CPG, rest = it / CPG;
       const int r = rest % MR, gg = rest / MR;
-      float sum = 0.0f;
-#pragma unroll
-      for (int q = 0; q < 16; ++q) sum = dot2_bf16(raw[i][q], 0x3F803F80u, sum);
-      // the group's sum: chunk sums of adjacent lanes, lower chunk first
-      if constexpr (CPG >= 2) sum += dpp<kDppXor1>(sum);
-      if constexpr (CPG >= 4) sum += dpp<kDppXor2>(sum);
-      if (it_raw < kUnits) {
-        unsigned char *dst = xp + ((gg * CPG + ch) * MR + r) * kQmmRow;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          uint32_t pr[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            // pair 4q + e = (x[8q + e], x[8q + e + 4])
-            pr[e] = __builtin_amdgcn_perm(raw[i][4 * q + 2 + (e >> 1)], raw[i][4 * q + (e >> 1)],
-                                          (e & 1) ? 0x07060302u : 0x05040100u);
-          }
-          *reinterpret_cast<uint4 *>(dst + q * 16) = make_uint4(pr[0], pr[1], pr[2], pr[3]);
-        }
-        if (ch == 0) xsum[gg * MR + r] = sum;
-      }
+      const uint4 v = raw[i];
+      float sum = dot2_bf16(v.x, 0x3F803F80u, 0.0f);
+      sum = dot2_bf16(v.y, 0x3F803F80u, sum);
+      sum = dot2_bf16(v.z, 0x3F803F80u, sum);
+      sum = dot2_bf16(v.w, 0x3F803F80u, sum);
+      // the group's sum: the quad's quarters, then the quads of the group's
+      // chunks (adjacent lanes)
+      sum += dpp<kDppXor1>(sum);
+      sum += dpp<kDppXor2>(sum);
+      if constexpr (CPG >= 2) sum += dpp<kDppHalfMirror>(sum);
+      if constexpr (CPG >= 4) sum += dpp<kDppRor8>(sum);
+      unsigned char *dst = xp + ((gg * CPG + ch) * MR + r) * kQmmRow + qq * 16;
+      // pair e = (x[e], x[e + 4]) of the piece's 8 values
+      *reinterpret_cast<uint4 *>(dst) = make_uint4(__builtin_amdgcn_perm(v.z, v.x, 0x05040100u),
+                                                   __builtin_amdgcn_perm(v.z, v.x, 0x07060302u),
+                                                   __builtin_amdgcn_perm(v.w, v.y, 0x05040100u),
+                                                   __builtin_amdgcn_perm(v.w, v.y, 0x07060302u));
+      if (ch == 0 && qq == 0) xsum[gg * MR + r] = sum;
     }
     __syncthreads();
 
@@ -247,8 +260,11 @@ __device__ __forceinline__ void qmm_accumulate(const uint32_t *__restrict__ w, c
           }
         }
         if constexpr (last) {                     // fold the group
-          const float s = bf16_to_f32(sa[cc / CPG]);
-          const float zc = fmaf(-kZc, s, bf16_to_f32(za[cc / CPG]));
+          constexpr int gg = cc / CPG;
+          const uint32_t szv = static_cast<uint32_t>(
+              __builtin_amdgcn_ds_bpermute((j + 16 * (gg % 4)) * 4, static_cast<int>(sz[gg / 4])));
+          const float s = __builtin_bit_cast(float, szv << 16);
+          const float zc = fmaf(-kZc, s, __builtin_bit_cast(float, szv & 0xFFFF0000u));
 #pragma unroll
           for (int t = 0; t < BM; ++t) {
             const float4 xg = *reinterpret_cast<const float4 *>(xsum + (cc / CPG) * MR + t * 16 + 4 * kb);

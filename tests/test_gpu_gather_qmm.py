@@ -61,6 +61,12 @@ def test_gather_qmm_parity(dev, bits, g):
     _check(dev, 8, 200, 1152, bits, g, T=48, top=2, seed=bits + g)
 
 
+@pytest.mark.parametrize("bits", (3, 5, 8))
+def test_gather_qmm_rows_off_16_byte_boundaries(dev, bits):
+    """K = 288 (9 chunks): 3- and 5-bit rows are not a multiple of 16 bytes."""
+    _check(dev, 4, 72, 288, bits, 32, T=32, top=2, seed=bits + 50)
+
+
 def test_gather_qmm_many_vectors_and_an_empty_expert(dev):
     """Expert 3 gets no pair; experts 0 and 1 get more than 64 vectors."""
     T, top, E = 160, 2, 6

@@ -60,6 +60,15 @@ def test_qmm_single_slice_launch(dev, bits):
     _check(32768, 256, 64, bits, 12, dev, seed=11)
 
 
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("K,g", [(288, 32), (320, 64), (384, 128)])
+def test_qmm_rows_off_16_byte_boundaries(dev, bits, K, g):
+    """K / 32 = 9, 10 or 12 chunks: for odd bit widths (and 2 or 6 bits at 9
+    chunks) a packed row is not a multiple of 16 bytes, so the rows start off
+    16-byte boundaries; the rest start on them with a partial 8-chunk block."""
+    _check(72, K, g, bits, 20, dev, seed=bits * 7 + K)
+
+
 @pytest.mark.parametrize("bits,M", [(4, 64), (4, 128), (8, 16), (2, 32), (6, 48)])
 def test_qmm_prefill_shapes(dev, bits, M):
     _check(4096, 4096, 64, bits, M, dev, seed=synth.SEED_W)
