@@ -292,7 +292,7 @@ int workspace_for(hipStream_t st, size_t bytes, void **out) {
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(st, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone)
       return fail(QMV_EUNSUPPORTED,
-                  "qmv: transpose=0 needs a %zu-byte workspace on this stream; make one call of "
+                  "qmv: this call needs a %zu-byte workspace on this stream; make one call of "
                   "this size (or larger) on the stream before capturing it", bytes);
     void *p = nullptr;
     if (hipMalloc(&p, bytes) != hipSuccess)

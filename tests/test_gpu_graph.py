@@ -98,3 +98,37 @@ def test_qvm_graph_replays_match_eager(dev):
         torch.cuda.synchronize()
         np.testing.assert_array_equal(bf16_to_np_bits(y), y_eager, err_msg=f"replay {rep}")
         del junk
+
+
+def test_qmm_graph_replays_match_eager(dev):
+    """The split-K matrix-core path (M = 32 rows of x) under capture: a
+    warm-up call sets up the stream's workspace; replays alternate with eager
+    calls on the capture stream and on another stream, and every replay must
+    reproduce the eager bits."""
+    import torch
+
+    import bit_affine_quantized_amd as q
+    M, N, K, g, bits = 32, 1024, 2048, 64, 4
+    w = _packed(N, K, bits, g, dev, seed=3)
+    x = to_dev_bf16(synth.activation_bf16((M, K), 7), dev)
+    side = torch.cuda.Stream()
+    y = torch.zeros((M, N), dtype=torch.bfloat16, device=dev)
+    with torch.cuda.stream(side):
+        q.qmv(x, *w, group_size=g, bits=bits, y=y)                       # warm-up
+    torch.cuda.synchronize()
+    y_eager = bf16_to_np_bits(y)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        q.qmv(x, *w, group_size=g, bits=bits, y=y)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        y.zero_()
+        junk = q.qmv(x, *w, group_size=g, bits=bits)                     # default stream
+        with torch.cuda.stream(side):
+            junk2 = q.qmv(x, *w, group_size=g, bits=bits)                # capture stream
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(bf16_to_np_bits(junk2), y_eager, err_msg=f"eager {rep}")
+        graph.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(bf16_to_np_bits(y), y_eager, err_msg=f"replay {rep}")
+        del junk, junk2
