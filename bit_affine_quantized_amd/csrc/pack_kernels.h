@@ -92,9 +92,12 @@ __device__ __forceinline__ uint16_t bf16_of_sum(float hi, float lo) {
 // contiguous run; all of a thread's loads are issued before its first
 // store.  A unit's E codes are E*b consecutive bits of its chunk (at most
 // 64, inside two consecutive words), read straight from memory: the 4 or 8
-// units of a chunk share its words through the cache.
+// units of a chunk share its words through the cache.  The output is
+// written with non-temporal stores: it is never read back by this kernel,
+// and streaming it past the cache measured 38.5 -> 35.5 us for 14336x4096
+// 4-bit -> bf16 (with 2 units per thread; 1 unit 46 us, 4 units 36.3 us).
 #ifndef QMV_DEQUANT_UNITS
-#define QMV_DEQUANT_UNITS 4
+#define QMV_DEQUANT_UNITS 2
 #endif
 constexpr int kDequantUnits = QMV_DEQUANT_UNITS;
 
@@ -147,14 +150,16 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t *__restrict
       l[e] = (p - (sum - b2)) + (zf - b2);
     }
     if constexpr (F32) {
-      reinterpret_cast<float4 *>(out)[t] = make_float4(h[0], h[1], h[2], h[3]);
+      typedef float f32x4v __attribute__((ext_vector_type(4)));
+      __builtin_nontemporal_store(f32x4v{h[0], h[1], h[2], h[3]}, reinterpret_cast<f32x4v *>(out) + t);
     } else {
       uint32_t o[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k)
         o[k] = static_cast<uint32_t>(bf16_of_sum(h[2 * k], l[2 * k])) |
                (static_cast<uint32_t>(bf16_of_sum(h[2 * k + 1], l[2 * k + 1])) << 16);
-      reinterpret_cast<uint4 *>(out)[t] = make_uint4(o[0], o[1], o[2], o[3]);
+      typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+      __builtin_nontemporal_store(u32x4v{o[0], o[1], o[2], o[3]}, reinterpret_cast<u32x4v *>(out) + t);
     }
   }
 }
