@@ -352,9 +352,10 @@ def workloads():
         n = f"moe_gather_64x2048x2048_b4_g64_t16_top8_{'sorted' if srt else 'unsorted'}"
         W[n] = make_moe(m["E"], m["N"], m["K"], m["bits"], m["group"],
                         m["tokens"], m["top_k"], srt, n)
-    # prefill-sized routing (64 vectors per expert): the matrix-core gather
-    n = "moe_gather_64x2048x2048_b4_g64_t512_top8_unsorted"
-    W[n] = make_moe(m["E"], m["N"], m["K"], m["bits"], m["group"], 512, m["top_k"], False, n)
+    # larger routings (8 and 64 vectors per expert): the matrix-core gather
+    for T in (64, 512):
+        n = f"moe_gather_64x2048x2048_b4_g64_t{T}_top8_unsorted"
+        W[n] = make_moe(m["E"], m["N"], m["K"], m["bits"], m["group"], T, m["top_k"], False, n)
     return W
 
 

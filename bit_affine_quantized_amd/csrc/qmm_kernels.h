@@ -409,9 +409,9 @@ constexpr int kGqmmWaves = QMV_GQMM_WAVES;
 constexpr int kGqmmThreads = kGqmmWaves * kWave;
 constexpr int kGqmmRowsPerWG = 16 * kGqmmWaves;
 
-template <int BITS, int CPG>
+template <int BITS, int CPG, int BM>
 __global__ __launch_bounds__(kGqmmThreads) void gather_qmm_kernel(GatherQmmArgs a) {
-  constexpr int BM = 4, MR = 64;
+  constexpr int MR = 16 * BM;                     // x vectors per slab
   constexpr int P = BITS == 8 ? 3 : 7 - BITS;
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int list[kGqmmListMax];

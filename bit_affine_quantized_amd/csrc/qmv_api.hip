@@ -226,38 +226,63 @@ int launch_gather_t(const qmvk::GatherArgs &a0, int64_t E, hipStream_t st) {
 }
 
 #ifndef QMV_GATHER_QMM_MIN
-#define QMV_GATHER_QMM_MIN 12     // mean x vectors per expert for the matrix-core gather
+// mean x vectors per expert from which gather_qmv uses the matrix cores (64
+// experts of 2048x2048 4-bit, top-8, on MI355X, matvec vs matrix cores: 4
+// per expert 64.6 vs 85.5 us, 6 per expert 84.7 vs 85.1, 8 per expert 103
+// vs 85.8, 10 per expert 121.7 vs 85.2)
+#define QMV_GATHER_QMM_MIN 8
 #endif
 
-template <int BITS, int CPG>
+template <int BITS, int CPG, int BM>
 int launch_gather_qmm_t(const qmvk::GatherQmmArgs &a0, int64_t E, hipStream_t st) {
   qmvk::GatherQmmArgs a = a0;
+  constexpr int MR = 16 * BM;
   const int64_t NB = (a.N + qmvk::kGqmmRowsPerWG - 1) / qmvk::kGqmmRowsPerWG;
-  // Slabs of 64 x vectors run in parallel workgroups: an expert routed more
-  // than 64 vectors would otherwise take its slabs one after another and set
+  // Slabs of MR x vectors run in parallel workgroups: an expert routed more
+  // than MR vectors would otherwise take its slabs one after another and set
   // the kernel's critical path.  1.5x the mean slab count per expert covers
   // the usual spread; an expert with more slabs loops over them.  (512 tokens
   // x top-8 over 64 experts on MI355X, ~64 vectors per expert.)
   const int64_t mean_vec = (a.P * a.M + E - 1) / E;
-  int64_t slabs = (3 * mean_vec + 127) / 128;
+  int64_t slabs = (3 * mean_vec + 2 * MR - 1) / (2 * MR);
   if (slabs < 1) slabs = 1;
   if (slabs > 8) slabs = 8;
   if (slabs * E * NB > 0x7FFFFFFF) return fail(QMV_EUNSUPPORTED, "gather_qmv: grid too large");
   a.slabs = static_cast<int>(slabs);
-  constexpr int lds = qmvk::qmm_lds_bytes<4>();
-  auto kern = qmvk::gather_qmm_kernel<BITS, CPG>;
+  constexpr int lds = qmvk::qmm_lds_bytes<BM>();
+  auto kern = qmvk::gather_qmm_kernel<BITS, CPG, BM>;
   allow_lds(kern, lds);
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(slabs * E * NB)), dim3(qmvk::kGqmmThreads), lds,
                      st, a);
   return check_launch("gather_qmv (matrix cores)");
 }
 
+// Slab height (m-tiles of 16 x vectors): the smallest whose one slab covers
+// 1.5x the mean vectors per expert.  Taller slabs stage and multiply
+// padding; shorter ones make most experts read their weights twice.
+// (64 experts of 2048x2048 4-bit, top-8, on MI355X, slabs of 16 / 32 / 64:
+// 8 per expert 85.8 / 99.5 / 106.7 us, 12 per expert 120 / 99.8 / 106.5,
+// 16 per expert 145 / 100.9 / 107.)
+#ifndef QMV_GQMM_BM
+#define QMV_GQMM_BM 0             // 0: chosen per call; 1, 2 or 4: fixed
+#endif
+template <int BITS, int CPG>
+int launch_gather_qmm_c(const qmvk::GatherQmmArgs &a, int64_t E, hipStream_t st) {
+  const int64_t mean_vec = (a.P * a.M + E - 1) / E;
+  const int bm = QMV_GQMM_BM ? QMV_GQMM_BM : (3 * mean_vec <= 2 * 16 ? 1 : 3 * mean_vec <= 2 * 32 ? 2 : 4);
+  switch (bm) {
+    case 1: return launch_gather_qmm_t<BITS, CPG, 1>(a, E, st);
+    case 2: return launch_gather_qmm_t<BITS, CPG, 2>(a, E, st);
+    default: return launch_gather_qmm_t<BITS, CPG, 4>(a, E, st);
+  }
+}
+
 template <int BITS>
 int launch_gather_qmm_g(int gshift, const qmvk::GatherQmmArgs &a, int64_t E, hipStream_t st) {
   switch (gshift) {
-    case 0: return launch_gather_qmm_t<BITS, 1>(a, E, st);
-    case 1: return launch_gather_qmm_t<BITS, 2>(a, E, st);
-    default: return launch_gather_qmm_t<BITS, 4>(a, E, st);
+    case 0: return launch_gather_qmm_c<BITS, 1>(a, E, st);
+    case 1: return launch_gather_qmm_c<BITS, 2>(a, E, st);
+    default: return launch_gather_qmm_c<BITS, 4>(a, E, st);
   }
 }
 
@@ -395,9 +420,11 @@ int run_qvm(const uint16_t *x, const uint32_t *w_q, const uint16_t *scales, cons
 
 // ------------------------------------------------------------------ qmm
 #ifndef QMV_QMM_MIN_M
-// x rows from which transpose=1 uses the matrix cores (4096x4096 4-bit on
-// MI355X: M = 8 slabs 11.7 us vs MFMA 16.9 us; M = 16 22.6 us vs 17.1 us)
-#define QMV_QMM_MIN_M 12
+// x rows from which transpose=1 uses the matrix cores: anything past one
+// 4-row slab (4096x4096 4-bit on MI355X, slabs vs matrix cores: M = 5
+// 9.75 vs 9.69 us, M = 6 10.2 vs 9.7, M = 8 11.2 vs 9.75, M = 11 16.2 vs
+// 9.9; 14336x4096 at M = 8: 25.1 vs 19.3)
+#define QMV_QMM_MIN_M 5
 #endif
 #ifndef QMV_QMM_WGS
 #define QMV_QMM_WGS 512           // split-K target: workgroups per launch

@@ -93,7 +93,7 @@ int qmv_pack(const float *w, int64_t N, int64_t K, int group_size, int bits,
  *                  stream first.  Calls on one stream share its workspace
  *                  (stream order serializes them).
  * x: bf16 [M, K].  y: [M, N], bf16 or fp32 per out_dtype.  M >= 1.  With
- * transpose = 1 and 12 or more rows of x the matrix cores are used (64-row
+ * transpose = 1 and 5 or more rows of x the matrix cores are used (64-row
  * slabs of x, W read once per slab).
  */
 int qmv(const uint16_t *x, const uint32_t *w_q, const uint16_t *scales,
@@ -141,7 +141,7 @@ int qmv_silu_gate_resid(const uint16_t *gate, const uint16_t *up,
  * non-decreasing; it may make the call faster and never changes the results
  * (every output is computed with the same arithmetic either way).
  * transpose must be 1 (else QMV_EUNSUPPORTED).  When the routed x vectors
- * average 12 or more per expert (P*M >= 12*E) the matrix cores are used.
+ * average 8 or more per expert (P*M >= 8*E) the matrix cores are used.
  * One expert's packed weight (N*K*bits/8 bytes) must be under 2 GiB (else
  * QMV_EUNSUPPORTED): it is addressed with 32-bit offsets.
  */
