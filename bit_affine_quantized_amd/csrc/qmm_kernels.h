@@ -153,8 +153,8 @@ __device__ __forceinline__ void qmm_accumulate(const uint32_t *__restrict__ w, c
   // span contracts codes 8v..8v+7 of every window.  One load per span
   // instead of one per chunk: fewer cache-line requests per byte of W
   // (4096x4096 4-bit g64: M = 16 12.2 -> 10.3 us, M = 64 19.5 -> 18.5 us).
-  // SPANS is off for the gathered product, where the same change measured
-  // 175 -> 217 us on the 512-token top-8 gather over 64 experts.
+  // The gathered product takes SPANS for its slabs of 16 and 32 vectors only
+  // (with 64-vector slabs it measured 175 -> 217 us).
   constexpr int SPAN = (SPANS && (BITS == 2 || BITS == 4 || BITS == 8) && CPG >= 2) ? CPG : 1;
   constexpr int kWinDw = SPAN > 1 ? SPAN * BITS / 4 : 1;   // dwords per lane window
   const uint32_t wspan = nrow * static_cast<uint32_t>(Kc * BITS * 4) + static_cast<uint32_t>(SPAN * BITS * kb);
@@ -406,6 +406,13 @@ constexpr int kGqmmListMax = 1024;
 #define QMV_GQMM_WAVES 8
 #endif
 constexpr int kGqmmWaves = QMV_GQMM_WAVES;
+#ifndef QMV_GQMM_SPAN_BM
+// Spans (one W window per group, as in the plain product) for slabs of 16
+// and 32 vectors, not 64: 8 vectors per expert 85.1 -> 64.8 us, 16 per
+// expert 100.8 -> 73.2 us, but 64 per expert 175 -> 217 us (64 experts of
+// 2048x2048 4-bit, top-8, on MI355X).
+#define QMV_GQMM_SPAN_BM 6        // bit BM set: spans in the gathered product with BM m-tiles
+#endif
 constexpr int kGqmmThreads = kGqmmWaves * kWave;
 constexpr int kGqmmRowsPerWG = 16 * kGqmmWaves;
 
@@ -497,7 +504,7 @@ __global__ __launch_bounds__(kGqmmThreads) void gather_qmm_kernel(GatherQmmArgs 
       __syncthreads();
       auto xoff = [&](int r, int c) { return rowoff[r] + static_cast<uint32_t>(c) * 64u; };
       f32x4_t acc[BM], accz[BM];
-      qmm_accumulate<BITS, BM, CPG, kGqmmWaves, false>(we, se, be, a.x, nrow, Kc, 0, Kc, xoff, smem, acc, accz);
+      qmm_accumulate<BITS, BM, CPG, kGqmmWaves, ((QMV_GQMM_SPAN_BM >> BM) & 1) != 0>(we, se, be, a.x, nrow, Kc, 0, Kc, xoff, smem, acc, accz);
 
       constexpr float kInvP = 1.0f / static_cast<float>(1 << P);
 #pragma unroll

@@ -228,9 +228,9 @@ int launch_gather_t(const qmvk::GatherArgs &a0, int64_t E, hipStream_t st) {
 #ifndef QMV_GATHER_QMM_MIN
 // mean x vectors per expert from which gather_qmv uses the matrix cores (64
 // experts of 2048x2048 4-bit, top-8, on MI355X, matvec vs matrix cores: 4
-// per expert 64.6 vs 85.5 us, 6 per expert 84.7 vs 85.1, 8 per expert 103
-// vs 85.8, 10 per expert 121.7 vs 85.2)
-#define QMV_GATHER_QMM_MIN 8
+// per expert 64.1 vs 65.7 us, 5 per expert 75.5 vs 65.3, 6 per expert 86.0
+// vs 65.8, 8 per expert 103 vs 64.8)
+#define QMV_GATHER_QMM_MIN 5
 #endif
 
 template <int BITS, int CPG, int BM>

@@ -141,7 +141,7 @@ int qmv_silu_gate_resid(const uint16_t *gate, const uint16_t *up,
  * non-decreasing; it may make the call faster and never changes the results
  * (every output is computed with the same arithmetic either way).
  * transpose must be 1 (else QMV_EUNSUPPORTED).  When the routed x vectors
- * average 8 or more per expert (P*M >= 8*E) the matrix cores are used.
+ * average 5 or more per expert (P*M >= 5*E) the matrix cores are used.
  * One expert's packed weight (N*K*bits/8 bytes) must be under 2 GiB (else
  * QMV_EUNSUPPORTED): it is addressed with 32-bit offsets.
  */
