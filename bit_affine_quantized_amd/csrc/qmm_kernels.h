@@ -152,9 +152,9 @@ __device__ __forceinline__ void qmm_accumulate(const uint32_t *__restrict__ w, c
   // SPAN * b * kb) from each span of SPAN = CPG chunks, and MFMA v of the
   // span contracts codes 8v..8v+7 of every window.  One load per span
   // instead of one per chunk: fewer cache-line requests per byte of W
-  // (4096x4096 4-bit g64: M = 16 12.2 -> 10.3 us, M = 64 19.5 -> 18.5 us).
-  // The gathered product takes SPANS for its slabs of 16 and 32 vectors only
-  // (with 64-vector slabs it measured 175 -> 217 us).
+  // (4096x4096 4-bit g64: M = 16 12.2 -> 10.3 us, M = 64 19.5 -> 18.5 us;
+  // gathered, 64 experts of 2048x2048, top-8: 8 vectors per expert 85.1 ->
+  // 64.8 us, 64 per expert 175.9 -> 152.7 us).
   constexpr int SPAN = (SPANS && (BITS == 2 || BITS == 4 || BITS == 8) && CPG >= 2) ? CPG : 1;
   constexpr int kWinDw = SPAN > 1 ? SPAN * BITS / 4 : 1;   // dwords per lane window
   const uint32_t wspan = nrow * static_cast<uint32_t>(Kc * BITS * 4) + static_cast<uint32_t>(SPAN * BITS * kb);
@@ -406,18 +406,16 @@ constexpr int kGqmmListMax = 1024;
 #define QMV_GQMM_WAVES 8
 #endif
 constexpr int kGqmmWaves = QMV_GQMM_WAVES;
-#ifndef QMV_GQMM_SPAN_BM
-// Spans (one W window per group, as in the plain product) for slabs of 16
-// and 32 vectors, not 64: 8 vectors per expert 85.1 -> 64.8 us, 16 per
-// expert 100.8 -> 73.2 us, but 64 per expert 175 -> 217 us (64 experts of
-// 2048x2048 4-bit, top-8, on MI355X).
-#define QMV_GQMM_SPAN_BM 6        // bit BM set: spans in the gathered product with BM m-tiles
-#endif
 constexpr int kGqmmThreads = kGqmmWaves * kWave;
 constexpr int kGqmmRowsPerWG = 16 * kGqmmWaves;
 
 template <int BITS, int CPG, int BM>
-__global__ __launch_bounds__(kGqmmThreads) void gather_qmm_kernel(GatherQmmArgs a) {
+// At least 4 waves per SIMD (at most 128 VGPRs): with 64-vector slabs the
+// kernel otherwise takes 129 and only one 8-wave workgroup fits per CU.
+// 8-bit codes (two MFMAs per chunk) would spill under that cap and keep the
+// compiler's choice.
+__global__ __launch_bounds__(kGqmmThreads) __attribute__((amdgpu_waves_per_eu(BITS == 8 ? 1 : 4)))
+void gather_qmm_kernel(GatherQmmArgs a) {
   constexpr int MR = 16 * BM;                     // x vectors per slab
   constexpr int P = BITS == 8 ? 3 : 7 - BITS;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -504,7 +502,7 @@ __global__ __launch_bounds__(kGqmmThreads) void gather_qmm_kernel(GatherQmmArgs 
       __syncthreads();
       auto xoff = [&](int r, int c) { return rowoff[r] + static_cast<uint32_t>(c) * 64u; };
       f32x4_t acc[BM], accz[BM];
-      qmm_accumulate<BITS, BM, CPG, kGqmmWaves, ((QMV_GQMM_SPAN_BM >> BM) & 1) != 0>(we, se, be, a.x, nrow, Kc, 0, Kc, xoff, smem, acc, accz);
+      qmm_accumulate<BITS, BM, CPG, kGqmmWaves, true>(we, se, be, a.x, nrow, Kc, 0, Kc, xoff, smem, acc, accz);
 
       constexpr float kInvP = 1.0f / static_cast<float>(1 << P);
 #pragma unroll
