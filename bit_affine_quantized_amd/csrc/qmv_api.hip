@@ -330,6 +330,18 @@ int workspace_for(hipStream_t st, size_t bytes, void **out) {
   return QMV_OK;
 }
 
+// y = the S slices of `part` added in slice order (one thread per output),
+// with the load batch sized to S.
+void launch_slice_reduce(const float *part, int S, int MVs, int M, int64_t N, int64_t y_ld, int out_f32,
+                         void *y, hipStream_t st) {
+  const int64_t outs = static_cast<int64_t>(M) * N;
+  const dim3 grid(static_cast<unsigned>((outs + 255) / 256)), block(256);
+  if (S <= 8) hipLaunchKernelGGL(qmvk::qvm_reduce_kernel<8>, grid, block, 0, st, part, S, MVs, M, N, y_ld, out_f32, y);
+  else if (S <= 16) hipLaunchKernelGGL(qmvk::qvm_reduce_kernel<16>, grid, block, 0, st, part, S, MVs, M, N, y_ld, out_f32, y);
+  else if (S <= 32) hipLaunchKernelGGL(qmvk::qvm_reduce_kernel<32>, grid, block, 0, st, part, S, MVs, M, N, y_ld, out_f32, y);
+  else hipLaunchKernelGGL(qmvk::qvm_reduce_kernel<64>, grid, block, 0, st, part, S, MVs, M, N, y_ld, out_f32, y);
+}
+
 #ifndef QMV_QVM_ROWS
 #define QMV_QVM_ROWS 4            // rows in flight per stream
 #endif
@@ -370,9 +382,7 @@ int launch_qvm_t(const qmvk::QvmArgs &a0, hipStream_t st) {
                      static_cast<size_t>(lds), st, a);
   if (int rc = check_launch("qmv (transpose=0)")) return rc;
   if (S > 1) {
-    const int64_t outs = static_cast<int64_t>(a.M) * a.N;
-    hipLaunchKernelGGL(qmvk::qvm_reduce_kernel, dim3(static_cast<unsigned>((outs + 255) / 256)),
-                       dim3(256), 0, st, a.part, a.S, MV, a.M, a.N, a.y_ld, a.out_f32, a.y);
+    launch_slice_reduce(a.part, a.S, MV, a.M, a.N, a.y_ld, a.out_f32, a.y, st);
     return check_launch("qmv (transpose=0) reduce");
   }
   return QMV_OK;
@@ -456,9 +466,7 @@ int launch_qmm_t(const qmvk::QmmArgs &a0, hipStream_t st) {
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(NB * S)), dim3(qmvk::kQmmThreads), lds, st, a);
   if (int rc = check_launch("qmv (matrix cores)")) return rc;
   if (S > 1) {
-    const int64_t outs = static_cast<int64_t>(a.M) * a.N;
-    hipLaunchKernelGGL(qmvk::qvm_reduce_kernel, dim3(static_cast<unsigned>((outs + 255) / 256)),
-                       dim3(256), 0, st, a.part, a.S, MR, a.M, a.N, a.y_ld, a.out_f32, a.y);
+    launch_slice_reduce(a.part, a.S, MR, a.M, a.N, a.y_ld, a.out_f32, a.y, st);
     return check_launch("qmv (matrix cores) reduce");
   }
   return QMV_OK;
