@@ -173,6 +173,38 @@ def test_qmv_workloads_full(dev, name, N, K, bits, g, M):
     check_t2(run_qmv(x, dw, ds, db, g, bits, dev, out_f32=True), ref, name)
 
 
+@pytest.mark.parametrize("bits", (3, 4, 8))
+@pytest.mark.parametrize("M", (2, 3, 4))
+def test_qmv_headline_matrix_decode_batch(dev, bits, M):
+    """The 14336x4096 g64 matrix at decode batch 2-4: more than 4096 rows and
+    2-4 rows of x run two rows per wave against a 2- or 4-vector slab (the
+    4-value lane butterfly at two vectors, the 8-value one at four); 8-bit
+    codes take the fp32-staged form.  Every output, both modes."""
+    N, K, g = 14336, 4096, 64
+    w, ow, os_, ob = packed(N, K, bits, g)
+    dw, ds, db = to_dev_u32(ow, dev), to_dev_bf16(os_, dev), to_dev_bf16(ob, dev)
+    x = synth.activation_bf16((M, K), seed=300 + M)
+    ref = oracle.qmv(x, ow, os_, ob, g, bits)
+    check_t1(run_qmv(x, dw, ds, db, g, bits, dev), ref, f"b{bits} M={M} bf16")
+    check_t2(run_qmv(x, dw, ds, db, g, bits, dev, out_f32=True), ref,
+             f"b{bits} M={M} f32")
+
+
+@pytest.mark.parametrize("bits", (2, 4, 5, 8))
+@pytest.mark.parametrize("M", (2, 4))
+def test_qmv_ragged_rows_past_4096(dev, bits, M):
+    """N = 4100 (past 4096, not a multiple of the two-row wave tile) and
+    K = 1536 (24 chunks: a partial first lane step), at 2 and 4 rows of x."""
+    N, K, g = 4100, 1536, 64
+    w = crafted_weight(N, K, seed=bits * 11 + M)
+    ow, os_, ob = oracle.quantize_pack(w, g, bits)
+    dw, ds, db = to_dev_u32(ow, dev), to_dev_bf16(os_, dev), to_dev_bf16(ob, dev)
+    x = synth.activation_bf16((M, K), seed=400 + M)
+    ref = oracle.qmv(x, ow, os_, ob, g, bits)
+    check_t1(run_qmv(x, dw, ds, db, g, bits, dev), ref, "bf16")
+    check_t2(run_qmv(x, dw, ds, db, g, bits, dev, out_f32=True), ref, "f32")
+
+
 # ---------------------------------------------------------------- fused FFN
 def _ffn_weights(dev, N=14336, K=4096, bits=8, g=64, down=True):
     wg = packed(N, K, bits, g, seed=synth.SEED_W)

@@ -354,3 +354,38 @@ def test_bf16_narrowing_matches_torch():
     ours = np.array([oracle.bf16_from_f32(float(t)) for t in v], np.uint16)
     ref = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy()
     np.testing.assert_array_equal(ours, ref.view(np.uint16))
+
+
+@pytest.mark.parametrize("M", (2, 3))
+def test_gather_rows_per_entry_brute_force(M):
+    """Gather with M > 1 rows per batch entry: x is [Bx, M, K], y is
+    [P, M, N], and y[p, m] is row m of x[lhs[p]] against expert rhs[p]
+    (quantized.h, adjust_matrix_offsets for the gather kernels: x moves by
+    the lhs batch stride M*K, the output slot by N*M).  Every y[p, m, n] is
+    an explicit dot product over the page-decoded weight.  Row m of each
+    batch entry is made distinctive (one-hot at a row-dependent column plus
+    noise) so that a wrong x or y stride changes the answer by at least one
+    whole weight."""
+    E, N, K, g, bits, Bx = 4, 6, 128, 32, 4, 3
+    w = np.stack([synth.weight((N, K), seed=40 + e) for e in range(E)])
+    packs = [oracle.quantize_pack(w[e], g, bits) for e in range(E)]
+    w_q = np.stack([p[0] for p in packs])
+    s16 = np.stack([p[1] for p in packs])
+    b16 = np.stack([p[2] for p in packs])
+    x = synth.activation_bf16((Bx, M, K), seed=77)
+    one = synth.f32_to_bf16_bits(np.array([64.0], np.float32))[0]
+    for bi in range(Bx):
+        for m in range(M):
+            x[bi, m, (5 * bi + 17 * m) % K] = one
+    lhs = np.array([2, 0, 1, 2, 0, 1, 1], np.uint32)
+    rhs = np.array([3, 3, 0, 1, 2, 0, 3], np.uint32)
+    y = oracle.gather_qmv(x, w_q, s16, b16, lhs, rhs, g, bits)
+    assert y.shape == (lhs.size, M, N)
+    for p in range(lhs.size):
+        W = _w_hat_pages(w_q[rhs[p]], s16[rhs[p]], b16[rhs[p]], K, g, bits)
+        for m in range(M):
+            xv = synth.bf16_bits_to_f32(x[lhs[p], m]).astype(np.float64)
+            for n in range(N):
+                ref = sum(W[n, k] * xv[k] for k in range(K))
+                assert abs(y[p, m, n] - ref) <= 1e-12 * (1.0 + abs(ref)), \
+                    (p, m, n, y[p, m, n], ref)
