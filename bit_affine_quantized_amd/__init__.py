@@ -16,7 +16,8 @@ import os
 
 __all__ = [
     "QmvError", "lib", "qmv_pack", "qmv", "qmv_gate_up", "qmv_silu_gate_resid",
-    "gather_qmv", "qmv_dequantize", "qmv_unpack_codes", "QMV_OK", "QMV_EINVAL",
+    "gather_qmv", "qmv_dequantize", "qmv_unpack_codes", "qmv_workspace_bytes",
+    "QMV_OK", "QMV_EINVAL",
     "QMV_EUNSUPPORTED", "QMV_EHIP", "QMV_OUT_BF16", "QMV_OUT_F32",
 ]
 
@@ -34,6 +35,9 @@ _I = ctypes.c_int
 SIGNATURES = {
     "qmv_pack": [_P, _I64, _I64, _I, _I, _P, _P, _P, _P],
     "qmv": [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _I, _I, _I, _P],
+    "qmv_workspace_bytes": [_I64, _I64, _I64, _I, _I, _I, _P],
+    "qmv_with_workspace": [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _I, _I, _I,
+                           _P, ctypes.c_size_t, _P],
     "qmv_gate_up": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I, _I, _P],
     "qmv_silu_gate_resid": [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I, _I, _I,
                             _P],
@@ -150,9 +154,22 @@ def _wq(t, name="w_q"):
     return t
 
 
+def qmv_workspace_bytes(M: int, N: int, K: int, group_size: int = 64,
+                        bits: int = 4, transpose: bool = True) -> int:
+    """Bytes of split-K workspace a qmv call of these sizes needs (0: none)."""
+    out = ctypes.c_size_t(0)
+    _call("qmv_workspace_bytes", M, N, K, group_size, bits,
+          1 if transpose else 0, ctypes.byref(out))
+    return int(out.value)
+
+
 def qmv(x, w_q, scales, biases, transpose: bool = True, group_size: int = 64,
-        bits: int = 4, out_dtype=None, y=None, stream=None):
-    """y = x @ W_hat^T for x bf16 [..., M, K] (batch dims flattened into M)."""
+        bits: int = 4, out_dtype=None, y=None, stream=None, workspace=None):
+    """y = x @ W_hat^T for x bf16 [..., M, K] (batch dims flattened into M).
+
+    ``workspace``: an optional device tensor of at least
+    ``qmv_workspace_bytes(...)`` bytes for the split-K paths; without it the
+    library takes a stream-ordered allocation for the call."""
     torch = _torch()
     _bits16(x, "x")
     _wq(w_q)
@@ -164,8 +181,15 @@ def qmv(x, w_q, scales, biases, transpose: bool = True, group_size: int = 64,
     code, dt = _out_code(out_dtype)
     if y is None:
         y = torch.empty((*x.shape[:-1], N), dtype=dt, device=x.device)
-    _call("qmv", _ptr(x), _ptr(w_q), _ptr(scales), _ptr(biases), _ptr(y), M,
-          N, K, group_size, bits, 1 if transpose else 0, code, _stream(stream))
+    args = (_ptr(x), _ptr(w_q), _ptr(scales), _ptr(biases), _ptr(y), M, N, K,
+            group_size, bits, 1 if transpose else 0, code)
+    if workspace is None:
+        _call("qmv", *args, _stream(stream))
+    else:
+        if not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous device tensor")
+        _call("qmv_with_workspace", *args, _ptr(workspace),
+              workspace.numel() * workspace.element_size(), _stream(stream))
     return y
 
 

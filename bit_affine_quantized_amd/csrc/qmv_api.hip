@@ -5,15 +5,12 @@
 
 #include <cstdarg>
 #include <cstdio>
-#include <map>
-#include <mutex>
 #include <string>
-#include <utility>
-#include <vector>
 
 #include "qmv.h"
 #include "pack_kernels.h"
 #include "qmv_kernels.h"
+#include "qmv_line_kernels.h"
 #include "qvm_kernels.h"
 #include "qmm_kernels.h"
 
@@ -131,11 +128,39 @@ int qmv_waves_per_block(int64_t lds) {
   return per_cu * 4 >= 32 ? 4 : 8;
 }
 
+// One x vector and at most two 64-lane chunk steps per row (K <= 4096): the
+// straight-line kernel (qmv_line_kernels.h), same shapes as the loop kernel.
+template <int BITS, int RPW, int WPB, int CPL>
+int launch_line_t(const qmvk::QmvArgs &a, int64_t lds, hipStream_t st) {
+  const int64_t rows = static_cast<int64_t>(a.nmat) * a.N;
+  const int64_t blocks = (rows + WPB * RPW - 1) / (WPB * RPW);
+  if (blocks > 0x7FFFFFFF) return fail(QMV_EUNSUPPORTED, "qmv: too many rows");
+  const bool full = (a.K / 32) == CPL * qmvk::kWave;
+  auto kern = full ? qmvk::qmv_line_kernel<BITS, RPW, WPB, CPL, true>
+                   : qmvk::qmv_line_kernel<BITS, RPW, WPB, CPL, false>;
+  allow_lds(kern, lds);
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(WPB * qmvk::kWave),
+                     static_cast<size_t>(lds), st, a);
+  return check_launch("qmv");
+}
+
+template <int BITS, int RPW, int WPB>
+int launch_line_cpl(const qmvk::QmvArgs &a, int64_t lds, hipStream_t st) {
+  if (a.K / 32 <= qmvk::kWave) return launch_line_t<BITS, RPW, WPB, 1>(a, lds, st);
+  return launch_line_t<BITS, RPW, WPB, 2>(a, lds, st);
+}
+
 template <int BITS, int MV, int XIN>
 int launch_qmv_t(const qmvk::QmvArgs &a, hipStream_t st) {
   constexpr bool PAIR = (BITS <= 6) && (XIN == qmvk::XIN_PLAIN);
   const int64_t Kc = a.K / 32;
   const int64_t lds = Kc * qmvk::chunk_stride<PAIR, (XIN == qmvk::XIN_SILU ? 1 : MV)>();
+  if constexpr (XIN == qmvk::XIN_PLAIN && MV == 1) {
+    if (Kc <= 2 * qmvk::kWave && !QMV_FORCE_WPB) {
+      if (static_cast<int64_t>(a.nmat) * a.N <= QMV_SMALL_ROWS) return launch_line_cpl<BITS, 1, 8>(a, lds, st);
+      return launch_line_cpl<BITS, kRpw, 4>(a, lds, st);
+    }
+  }
   if constexpr (XIN == qmvk::XIN_PLAIN) {
     if (static_cast<int64_t>(a.nmat) * a.N <= QMV_SMALL_ROWS && !QMV_FORCE_WPB)
       return launch_qmv_wpb<BITS, MV, XIN, 8, 1>(a, lds, st);
@@ -296,40 +321,33 @@ int launch_unpack_t(const uint32_t *w_q, int64_t N, int64_t K, uint8_t *codes, h
   return check_launch("qmv_unpack_codes");
 }
 
-// ------------------------------------------------------------------ qvm
-// Workspace of the split-K qvm (its partial sums): per (device, stream),
-// grown on demand and held until the process ends.  A buffer that is
-// outgrown is kept, not freed, so a HIP graph captured with it stays valid.
-struct Workspace {
+// ------------------------------------------------------------------ workspace
+// The split-K paths (transpose = 0, and 5 or more rows of x on the matrix
+// cores) write the S slices' fp32 partial sums to a workspace that a second
+// kernel adds in slice order.  The workspace always belongs to one call:
+// qmv_with_workspace takes it as an argument and qmv takes a stream-ordered
+// allocation that it frees on the same stream.  In sizing mode nothing is launched and the
+// largest size any launch of the call needs is recorded.
+struct Ws {
   void *ptr = nullptr;
   size_t bytes = 0;
+  bool sizing = false;
+  size_t need = 0;
 };
-std::mutex g_ws_mu;
-std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
-std::vector<void *> g_ws_retired;
 
-int workspace_for(hipStream_t st, size_t bytes, void **out) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return fail(QMV_EHIP, "qmv: hipGetDevice failed");
-  std::lock_guard<std::mutex> lock(g_ws_mu);
-  Workspace &w = g_ws[{dev, st}];
-  if (w.bytes < bytes) {
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(st, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone)
-      return fail(QMV_EUNSUPPORTED,
-                  "qmv: this call needs a %zu-byte workspace on this stream; make one call of "
-                  "this size (or larger) on the stream before capturing it", bytes);
-    void *p = nullptr;
-    if (hipMalloc(&p, bytes) != hipSuccess)
-      return fail(QMV_EHIP, "qmv: workspace allocation of %zu bytes failed", bytes);
-    if (w.ptr) g_ws_retired.push_back(w.ptr);
-    w.ptr = p;
-    w.bytes = bytes;
+int take_workspace(Ws &ws, size_t bytes, float **out) {
+  if (ws.sizing) {
+    if (bytes > ws.need) ws.need = bytes;
+    return QMV_OK;
   }
-  *out = w.ptr;
+  if (ws.ptr == nullptr || ws.bytes < bytes)
+    return fail(QMV_EINVAL, "qmv: this call needs a %zu-byte workspace, %zu given (qmv_workspace_bytes "
+                "reports the size)", bytes, ws.ptr ? ws.bytes : static_cast<size_t>(0));
+  *out = static_cast<float *>(ws.ptr);
   return QMV_OK;
 }
 
+// ------------------------------------------------------------------ qvm
 // y = the S slices of `part` added in slice order (one thread per output),
 // with the load batch sized to S.
 void launch_slice_reduce(const float *part, int S, int MVs, int M, int64_t N, int64_t y_ld, int out_f32,
@@ -351,7 +369,7 @@ void launch_slice_reduce(const float *part, int S, int MVs, int M, int64_t N, in
 constexpr int kQvmRows = QMV_QVM_ROWS;
 
 template <int BITS, int MV>
-int launch_qvm_t(const qmvk::QvmArgs &a0, hipStream_t st) {
+int launch_qvm_t(const qmvk::QvmArgs &a0, Ws &ws, hipStream_t st) {
   qmvk::QvmArgs a = a0;
   const int64_t Nc = a.N / 32;
   const int64_t CB = (Nc + qmvk::kQvmC - 1) / qmvk::kQvmC;
@@ -372,10 +390,9 @@ int launch_qvm_t(const qmvk::QvmArgs &a0, hipStream_t st) {
   a.S = static_cast<int>(S);
   a.ks = static_cast<int>(ks);
   if (S > 1) {
-    void *ws = nullptr;
-    if (int rc = workspace_for(st, static_cast<size_t>(S) * MV * a.N * 4, &ws)) return rc;
-    a.part = static_cast<float *>(ws);
+    if (int rc = take_workspace(ws, static_cast<size_t>(S) * MV * a.N * 4, &a.part)) return rc;
   }
+  if (ws.sizing) return QMV_OK;
   auto kern = qmvk::qvm_kernel<BITS, MV, kQvmRows>;
   allow_lds(kern, lds);
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(CB * S)), dim3(qmvk::kQvmWaves * qmvk::kWave),
@@ -389,14 +406,14 @@ int launch_qvm_t(const qmvk::QvmArgs &a0, hipStream_t st) {
 }
 
 template <int MV>
-int launch_qvm_bits(int bits, const qmvk::QvmArgs &a, hipStream_t st) {
+int launch_qvm_bits(int bits, const qmvk::QvmArgs &a, Ws &ws, hipStream_t st) {
   switch (bits) {
-    case 2: return launch_qvm_t<2, MV>(a, st);
-    case 3: return launch_qvm_t<3, MV>(a, st);
-    case 4: return launch_qvm_t<4, MV>(a, st);
-    case 5: return launch_qvm_t<5, MV>(a, st);
-    case 6: return launch_qvm_t<6, MV>(a, st);
-    case 8: return launch_qvm_t<8, MV>(a, st);
+    case 2: return launch_qvm_t<2, MV>(a, ws, st);
+    case 3: return launch_qvm_t<3, MV>(a, ws, st);
+    case 4: return launch_qvm_t<4, MV>(a, ws, st);
+    case 5: return launch_qvm_t<5, MV>(a, ws, st);
+    case 6: return launch_qvm_t<6, MV>(a, ws, st);
+    case 8: return launch_qvm_t<8, MV>(a, ws, st);
   }
   return fail(QMV_EINVAL, "bits=%d", bits);
 }
@@ -404,7 +421,7 @@ int launch_qvm_bits(int bits, const qmvk::QvmArgs &a, hipStream_t st) {
 // y = x @ W_hat with W packed [K, N] along N: slabs of up to 4 vectors.
 int run_qvm(const uint16_t *x, const uint32_t *w_q, const uint16_t *scales, const uint16_t *biases,
             void *y, int64_t M, int64_t N, int64_t K, int group_size, int bits, int out_f32,
-            hipStream_t st) {
+            Ws &ws, hipStream_t st) {
   for (int64_t m0 = 0; m0 < M; m0 += 4) {
     qmvk::QvmArgs a{};
     const int64_t nv = M - m0 < 4 ? M - m0 : 4;
@@ -420,9 +437,9 @@ int run_qvm(const uint16_t *x, const uint32_t *w_q, const uint16_t *scales, cons
     a.M = static_cast<int>(nv);
     a.gshift = gshift_of(group_size);
     a.out_f32 = out_f32;
-    const int rc = nv == 1 ? launch_qvm_bits<1>(bits, a, st)
-                 : nv == 2 ? launch_qvm_bits<2>(bits, a, st)
-                           : launch_qvm_bits<4>(bits, a, st);
+    const int rc = nv == 1 ? launch_qvm_bits<1>(bits, a, ws, st)
+                 : nv == 2 ? launch_qvm_bits<2>(bits, a, ws, st)
+                           : launch_qvm_bits<4>(bits, a, ws, st);
     if (rc) return rc;
   }
   return ok();
@@ -441,7 +458,7 @@ int run_qvm(const uint16_t *x, const uint32_t *w_q, const uint16_t *scales, cons
 #endif
 
 template <int BITS, int BM, int CPG>
-int launch_qmm_t(const qmvk::QmmArgs &a0, hipStream_t st) {
+int launch_qmm_t(const qmvk::QmmArgs &a0, Ws &ws, hipStream_t st) {
   qmvk::QmmArgs a = a0;
   constexpr int MR = 16 * BM;
   const int64_t Kc = a.K / 32;
@@ -456,10 +473,9 @@ int launch_qmm_t(const qmvk::QmmArgs &a0, hipStream_t st) {
   a.S = static_cast<int>(S);
   a.cps = static_cast<int>(cps);
   if (S > 1) {
-    void *ws = nullptr;
-    if (int rc = workspace_for(st, static_cast<size_t>(S) * MR * a.N * 4, &ws)) return rc;
-    a.part = static_cast<float *>(ws);
+    if (int rc = take_workspace(ws, static_cast<size_t>(S) * MR * a.N * 4, &a.part)) return rc;
   }
+  if (ws.sizing) return QMV_OK;
   constexpr int lds = qmvk::qmm_lds_bytes<BM>();
   auto kern = qmvk::qmm_kernel<BITS, BM, CPG>;
   allow_lds(kern, lds);
@@ -473,28 +489,28 @@ int launch_qmm_t(const qmvk::QmmArgs &a0, hipStream_t st) {
 }
 
 template <int BITS, int CPG>
-int launch_qmm_bm(int bm, const qmvk::QmmArgs &a, hipStream_t st) {
+int launch_qmm_bm(int bm, const qmvk::QmmArgs &a, Ws &ws, hipStream_t st) {
   switch (bm) {
-    case 1: return launch_qmm_t<BITS, 1, CPG>(a, st);
-    case 2: return launch_qmm_t<BITS, 2, CPG>(a, st);
-    case 3: return launch_qmm_t<BITS, 3, CPG>(a, st);
-    default: return launch_qmm_t<BITS, 4, CPG>(a, st);
+    case 1: return launch_qmm_t<BITS, 1, CPG>(a, ws, st);
+    case 2: return launch_qmm_t<BITS, 2, CPG>(a, ws, st);
+    case 3: return launch_qmm_t<BITS, 3, CPG>(a, ws, st);
+    default: return launch_qmm_t<BITS, 4, CPG>(a, ws, st);
   }
 }
 
 template <int BITS>
-int launch_qmm_g(int bm, const qmvk::QmmArgs &a, hipStream_t st) {
+int launch_qmm_g(int bm, const qmvk::QmmArgs &a, Ws &ws, hipStream_t st) {
   switch (a.gshift) {
-    case 0: return launch_qmm_bm<BITS, 1>(bm, a, st);
-    case 1: return launch_qmm_bm<BITS, 2>(bm, a, st);
-    default: return launch_qmm_bm<BITS, 4>(bm, a, st);
+    case 0: return launch_qmm_bm<BITS, 1>(bm, a, ws, st);
+    case 1: return launch_qmm_bm<BITS, 2>(bm, a, ws, st);
+    default: return launch_qmm_bm<BITS, 4>(bm, a, ws, st);
   }
 }
 
 // y = x @ W_hat^T for many rows of x: slabs of up to 64 rows on the matrix cores.
 int run_qmm(const uint16_t *x, const uint32_t *w_q, const uint16_t *scales, const uint16_t *biases,
             void *y, int64_t M, int64_t N, int64_t K, int group_size, int bits, int out_f32,
-            hipStream_t st) {
+            Ws &ws, hipStream_t st) {
   for (int64_t m0 = 0; m0 < M; m0 += 64) {
     const int64_t rows = M - m0 < 64 ? M - m0 : 64;
     qmvk::QmmArgs a{};
@@ -513,12 +529,12 @@ int run_qmm(const uint16_t *x, const uint32_t *w_q, const uint16_t *scales, cons
     const int bm = static_cast<int>((rows + 15) / 16);
     int rc;
     switch (bits) {
-      case 2: rc = launch_qmm_g<2>(bm, a, st); break;
-      case 3: rc = launch_qmm_g<3>(bm, a, st); break;
-      case 4: rc = launch_qmm_g<4>(bm, a, st); break;
-      case 5: rc = launch_qmm_g<5>(bm, a, st); break;
-      case 6: rc = launch_qmm_g<6>(bm, a, st); break;
-      default: rc = launch_qmm_g<8>(bm, a, st); break;
+      case 2: rc = launch_qmm_g<2>(bm, a, ws, st); break;
+      case 3: rc = launch_qmm_g<3>(bm, a, ws, st); break;
+      case 4: rc = launch_qmm_g<4>(bm, a, ws, st); break;
+      case 5: rc = launch_qmm_g<5>(bm, a, ws, st); break;
+      case 6: rc = launch_qmm_g<6>(bm, a, ws, st); break;
+      default: rc = launch_qmm_g<8>(bm, a, ws, st); break;
     }
     if (rc) return rc;
   }
@@ -596,41 +612,54 @@ int qmv_dequantize(const uint32_t *w_q, const uint16_t *scales, const uint16_t *
   }
 }
 
-int qmv(const uint16_t *x, const uint32_t *w_q, const uint16_t *scales, const uint16_t *biases,
-        void *y, int64_t M, int64_t N, int64_t K, int group_size, int bits, int transpose,
-        int out_dtype, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// qmv with its workspace supplied (or, in sizing mode, only measured).  In
+// sizing mode no pointer is dereferenced or checked and nothing is launched.
+int qmv_impl(const uint16_t *x, const uint32_t *w_q, const uint16_t *scales, const uint16_t *biases,
+             void *y, int64_t M, int64_t N, int64_t K, int group_size, int bits, int transpose,
+             int out_dtype, Ws &ws, hipStream_t st) {
+  const bool ptrs = !ws.sizing;
   if (transpose != 0 && transpose != 1)
     return fail(QMV_EINVAL, "qmv: transpose=%d must be 0 or 1", transpose);
   // the packed (group) axis is K for transpose = 1 and N for transpose = 0
   if (int rc = transpose ? check_common("qmv", N, K, group_size, bits)
                          : check_shape("qmv (transpose=0)", K, "K", N, "N", group_size, bits)) return rc;
   if (M <= 0) return fail(QMV_EINVAL, "qmv: M=%lld must be positive", (long long)M);
-  if (!x || !w_q || !scales || !biases || !y) return fail(QMV_EINVAL, "qmv: null pointer argument");
+  if (ptrs && (!x || !w_q || !scales || !biases || !y)) return fail(QMV_EINVAL, "qmv: null pointer argument");
   if (out_dtype != QMV_OUT_BF16 && out_dtype != QMV_OUT_F32)
     return fail(QMV_EINVAL, "qmv: out_dtype=%d unknown", out_dtype);
   if (transpose == 0) {
-    if (int rc = check_aligned("qmv", w_q, "w_q")) return rc;
+    if (ptrs) {
+      if (int rc = check_aligned("qmv", w_q, "w_q")) return rc;
+    }
     if (K > (int64_t(1) << 30) || M > (int64_t(1) << 30))
       return fail(QMV_EUNSUPPORTED, "qmv: transpose=0 with K or M too large");
-    return run_qvm(x, w_q, scales, biases, y, M, N, K, group_size, bits, out_dtype == QMV_OUT_F32,
-                   static_cast<hipStream_t>(stream));
+    if (int rc = run_qvm(x, w_q, scales, biases, y, M, N, K, group_size, bits, out_dtype == QMV_OUT_F32, ws, st))
+      return rc;
+    return ok();
   }
-  if (int rc = check_aligned("qmv", x, "x")) return rc;
-  if (int rc = check_aligned("qmv", w_q, "w_q")) return rc;
+  if (ptrs) {
+    if (int rc = check_aligned("qmv", x, "x")) return rc;
+    if (int rc = check_aligned("qmv", w_q, "w_q")) return rc;
+  }
   if (M >= QMV_QMM_MIN_M && N * K * bits / 8 < (int64_t(1) << 32) &&
       N * (K / group_size) * 2 < (int64_t(1) << 32) && 64 * K * 2 < (int64_t(1) << 32)) {
     // (the matrix-core kernel addresses W, scales and biases and a 64-row
     // slab of x with 32-bit byte offsets)
     if (M > (int64_t(1) << 30)) return fail(QMV_EUNSUPPORTED, "qmv: M=%lld too large", (long long)M);
-    return run_qmm(x, w_q, scales, biases, y, M, N, K, group_size, bits, out_dtype == QMV_OUT_F32,
-                   static_cast<hipStream_t>(stream));
+    if (int rc = run_qmm(x, w_q, scales, biases, y, M, N, K, group_size, bits, out_dtype == QMV_OUT_F32, ws, st))
+      return rc;
+    return ok();
   }
   const int mv_max = qmv_lds_bytes(bits, 4, K) <= kMaxLds ? 4
                    : qmv_lds_bytes(bits, 2, K) <= kMaxLds ? 2
                    : qmv_lds_bytes(bits, 1, K) <= kMaxLds ? 1 : 0;
   if (mv_max == 0)
     return fail(QMV_EUNSUPPORTED, "qmv: K=%lld too large for one workgroup's staged x", (long long)K);
-  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (ws.sizing) return ok();   // the matvec slabs need no workspace
   const size_t esz = out_dtype == QMV_OUT_F32 ? 4 : 2;
   for (int64_t m0 = 0; m0 < M; m0 += mv_max) {
     const int mv = static_cast<int>(M - m0 < mv_max ? M - m0 : mv_max);
@@ -652,6 +681,60 @@ int qmv(const uint16_t *x, const uint32_t *w_q, const uint16_t *scales, const ui
     if (rc) return rc;
   }
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int qmv_workspace_bytes(int64_t M, int64_t N, int64_t K, int group_size, int bits, int transpose,
+                        size_t *bytes) {
+  if (!bytes) return fail(QMV_EINVAL, "qmv_workspace_bytes: null bytes pointer");
+  Ws ws;
+  ws.sizing = true;
+  if (int rc = qmv_impl(nullptr, nullptr, nullptr, nullptr, nullptr, M, N, K, group_size, bits, transpose,
+                        QMV_OUT_BF16, ws, nullptr))
+    return rc;
+  *bytes = ws.need;
+  return ok();
+}
+
+int qmv_with_workspace(const uint16_t *x, const uint32_t *w_q, const uint16_t *scales,
+                       const uint16_t *biases, void *y, int64_t M, int64_t N, int64_t K, int group_size,
+                       int bits, int transpose, int out_dtype, void *workspace, size_t workspace_bytes,
+                       void *stream) {
+  if (workspace && !aligned16(workspace))
+    return fail(QMV_EINVAL, "qmv_with_workspace: workspace must be 16-byte aligned");
+  Ws ws;
+  ws.ptr = workspace;
+  ws.bytes = workspace ? workspace_bytes : 0;
+  return qmv_impl(x, w_q, scales, biases, y, M, N, K, group_size, bits, transpose, out_dtype, ws,
+                  static_cast<hipStream_t>(stream));
+}
+
+int qmv(const uint16_t *x, const uint32_t *w_q, const uint16_t *scales, const uint16_t *biases,
+        void *y, int64_t M, int64_t N, int64_t K, int group_size, int bits, int transpose,
+        int out_dtype, void *stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Ws sizing;
+  sizing.sizing = true;
+  if (int rc = qmv_impl(x, w_q, scales, biases, y, M, N, K, group_size, bits, transpose, out_dtype, sizing, st))
+    return rc;
+  Ws ws;
+  if (sizing.need > 0) {
+    // a stream-ordered allocation for this call only, freed on the same
+    // stream after the call's kernels (no state kept between calls)
+    if (hipMallocAsync(&ws.ptr, sizing.need, st) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(QMV_EHIP, "qmv: stream-ordered allocation of the %zu-byte split-K workspace failed "
+                  "(qmv_with_workspace takes a caller-owned workspace)", sizing.need);
+    }
+    ws.bytes = sizing.need;
+  }
+  const int rc = qmv_impl(x, w_q, scales, biases, y, M, N, K, group_size, bits, transpose, out_dtype, ws, st);
+  if (ws.ptr && hipFreeAsync(ws.ptr, st) != hipSuccess && rc == QMV_OK)
+    return fail(QMV_EHIP, "qmv: freeing the split-K workspace failed");
+  return rc;
 }
 
 int qmv_gate_up(const uint16_t *x, const uint32_t *wg, const uint16_t *sg, const uint16_t *bg,

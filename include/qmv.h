@@ -21,8 +21,10 @@
  *
  * Conventions for every entry point:
  *   - All array pointers are DEVICE pointers owned by the caller; the library
- *     never allocates, frees or keeps them.  bf16 values travel as uint16 bit
- *     patterns.  `stream` is a hipStream_t (NULL = the legacy default stream).
+ *     never frees or keeps them.  The only allocation is qmv's stream-ordered
+ *     split-K workspace, which lives for one call (see qmv).  bf16 values
+ *     travel as uint16 bit patterns.  `stream` is a hipStream_t (NULL = the
+ *     legacy default stream).
  *   - Calls are asynchronous on `stream`: they enqueue kernels and return.
  *     Results are visible after the stream is synchronized.
  *   - Arguments are validated on the host before any HIP call.  A bad size,
@@ -44,6 +46,7 @@
 #ifndef QMV_H
 #define QMV_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -78,27 +81,52 @@ int qmv_pack(const float *w, int64_t N, int64_t K, int group_size, int bits,
  * qmv -- quantized matmul at decode batch sizes (mlx/ops.cpp quantized_matmul;
  * quantized.h qmv_fast / qmv kernels).
  *   transpose = 1: W packed [N, K]; y[m, n] = sum_k x[m, k] * w_hat[n, k].
- *                  K must be a multiple of group_size.  The W stream is read
- *                  once per slab of up to 4 rows of x.
+ *                  K must be a multiple of group_size.  Up to 4 rows of x:
+ *                  the W stream is read once per slab of up to 4 rows.  With
+ *                  5 or more rows the matrix cores are used (64-row slabs of
+ *                  x, W read once per slab) and K is split into slices.
  *   transpose = 0: W packed [K, N] (groups along N, quantized.h qvm and its
  *                  split-K variant); y[m, n] = sum_k x[m, k] * w_hat[k, n].
  *                  N must be a multiple of group_size; W is read once per
- *                  slab of up to 2 rows of x.  K is split into slices whose
- *                  partial sums go to a library-held workspace (per device
- *                  and stream, allocated on first use, kept until the
- *                  process ends) and are added in a fixed order, so results
- *                  are reproducible.  Under HIP graph capture a call that
- *                  would need a new or larger workspace returns
- *                  QMV_EUNSUPPORTED: make one eager call of that size on the
- *                  stream first.  Calls on one stream share its workspace
- *                  (stream order serializes them).
- * x: bf16 [M, K].  y: [M, N], bf16 or fp32 per out_dtype.  M >= 1.  With
- * transpose = 1 and 5 or more rows of x the matrix cores are used (64-row
- * slabs of x, W read once per slab).
+ *                  slab of up to 4 rows of x, and K is split into slices.
+ *   Split-K calls write the slices' fp32 partial sums to a workspace and add
+ *   them in slice order in a second kernel, so results are reproducible.
+ *   qmv takes that workspace as a stream-ordered allocation
+ *   (hipMallocAsync) for the call and frees it on the same stream after the
+ *   call's kernels (hipFreeAsync); the library keeps no state between
+ *   calls.  Callers that cannot allocate use qmv_with_workspace.
+ *   qmv_workspace_bytes reports whether a call splits K.
+ * x: bf16 [M, K].  y: [M, N], bf16 or fp32 per out_dtype.  M >= 1.
+ * x and w_q must be 16-byte aligned (transpose = 1; w_q for transpose = 0).
  */
 int qmv(const uint16_t *x, const uint32_t *w_q, const uint16_t *scales,
         const uint16_t *biases, void *y, int64_t M, int64_t N, int64_t K,
         int group_size, int bits, int transpose, int out_dtype, void *stream);
+
+/*
+ * qmv_workspace_bytes -- the workspace (bytes) that qmv_with_workspace needs
+ * for a call of these sizes: the split-K partial sums, S slices x (rows of x
+ * in one slab) x N fp32 values; 0 when the call does not split K.  Validates
+ * the sizes like qmv (QMV_EINVAL / QMV_EUNSUPPORTED) and touches no device.
+ */
+int qmv_workspace_bytes(int64_t M, int64_t N, int64_t K, int group_size,
+                        int bits, int transpose, size_t *bytes);
+
+/*
+ * qmv_with_workspace -- qmv with a caller-owned device workspace of
+ * workspace_bytes bytes (16-byte aligned; NULL allowed when
+ * qmv_workspace_bytes reports 0).  QMV_EINVAL if it is smaller than the call
+ * needs.  The library allocates nothing.  The workspace is in use until the
+ * call's kernels on `stream` have finished: calls that may run at the same
+ * time (other streams, graphs replayed concurrently) need workspaces of
+ * their own.  A HIP graph that captures this call keeps the workspace
+ * pointer.  Results are bit-identical to qmv's.
+ */
+int qmv_with_workspace(const uint16_t *x, const uint32_t *w_q,
+                       const uint16_t *scales, const uint16_t *biases,
+                       void *y, int64_t M, int64_t N, int64_t K,
+                       int group_size, int bits, int transpose, int out_dtype,
+                       void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * qmv_gate_up -- dual-output matvec over one input in ONE launch

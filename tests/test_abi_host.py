@@ -146,3 +146,48 @@ def test_error_message_clears_on_success_path_is_thread_local():
     t.join()
     assert seen["msg"] == ""
     assert "bits=7" in L.qmv_last_error().decode()
+
+
+def _ws_bytes(M, N, K, g=64, bits=4, transpose=1):
+    out = ctypes.c_size_t(12345)
+    rc = q.lib().qmv_workspace_bytes(M, N, K, g, bits, transpose,
+                                      ctypes.byref(out))
+    return rc, int(out.value)
+
+
+@pytest.mark.parametrize("M", (1, 2, 3, 4))
+def test_workspace_none_for_matvec_slabs(M):
+    assert _ws_bytes(M, 14336, 4096) == (q.QMV_OK, 0)
+
+
+@pytest.mark.parametrize("M,N,K,transpose", [(1, 4096, 4096, 0), (4, 4096, 4096, 0),
+                                             (8, 4096, 4096, 1), (64, 4096, 4096, 1),
+                                             (300, 1024, 2048, 1)])
+def test_workspace_split_k_sizes(M, N, K, transpose):
+    rc, nbytes = _ws_bytes(M, N, K, transpose=transpose)
+    assert rc == q.QMV_OK
+    # S slices x (rows of x in the largest slab) x N fp32 partial sums
+    assert nbytes > 0 and nbytes % (4 * N) == 0
+    rows = min(M, 4) if transpose == 0 else 16 * ((min(M, 64) + 15) // 16)
+    assert (nbytes // (4 * N)) % rows == 0
+
+
+def test_workspace_bytes_validates_sizes():
+    rc, _ = _ws_bytes(1, 16, 96)           # K not a multiple of 64
+    assert rc == q.QMV_EINVAL
+    rc, _ = _ws_bytes(0, 16, 64)
+    assert rc == q.QMV_EINVAL
+    assert q.lib().qmv_workspace_bytes(1, 16, 64, 64, 4, 1, None) == q.QMV_EINVAL
+
+
+def test_with_workspace_too_small_is_rejected_before_any_launch():
+    rc, need = _ws_bytes(1, 4096, 4096, transpose=0)
+    assert rc == q.QMV_OK and need > 0
+    L = q.lib()
+    rc = L.qmv_with_workspace(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4096, 4096, 64, 4,
+                              0, 0, FAKE, need - 16, None)
+    assert rc == q.QMV_EINVAL
+    assert b"workspace" in L.qmv_last_error()
+    rc = L.qmv_with_workspace(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4096, 4096, 64, 4,
+                              0, 0, ctypes.c_void_p(0x1008), need, None)
+    assert rc == q.QMV_EINVAL and b"aligned" in L.qmv_last_error()

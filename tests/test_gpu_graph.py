@@ -71,8 +71,9 @@ def test_ffn_graph_replays_match_eager(dev):
 
 
 def test_qvm_graph_replays_match_eager(dev):
-    """transpose = 0 under capture: a warm-up call first sets up the stream's
-    split-K workspace, then every replay must reproduce the eager bits."""
+    """transpose = 0 (split K) under capture: the call's stream-ordered
+    workspace becomes part of the graph, and every replay must reproduce the
+    eager bits."""
     import torch
 
     import bit_affine_quantized_amd as q
@@ -101,10 +102,9 @@ def test_qvm_graph_replays_match_eager(dev):
 
 
 def test_qmm_graph_replays_match_eager(dev):
-    """The split-K matrix-core path (M = 32 rows of x) under capture: a
-    warm-up call sets up the stream's workspace; replays alternate with eager
-    calls on the capture stream and on another stream, and every replay must
-    reproduce the eager bits."""
+    """The split-K matrix-core path (M = 32 rows of x) under capture: replays
+    alternate with eager calls on the capture stream and on another stream,
+    and every replay must reproduce the eager bits."""
     import torch
 
     import bit_affine_quantized_amd as q
@@ -132,3 +132,94 @@ def test_qmm_graph_replays_match_eager(dev):
         torch.cuda.synchronize()
         np.testing.assert_array_equal(bf16_to_np_bits(y), y_eager, err_msg=f"replay {rep}")
         del junk, junk2
+
+
+def _split_k_cases(dev):
+    """Two split-K calls with different inputs: transpose = 0 (qvm) and 32
+    rows of x on the matrix cores."""
+    K, N, g, bits = 2048, 1024, 64, 4
+    wv = oracle.quantize_pack(synth.weight((K, N), 11), g, bits)
+    wm = oracle.quantize_pack(synth.weight((N, K), 12), g, bits)
+    xv = synth.activation_bf16((2, K), 21)
+    xm = synth.activation_bf16((32, K), 22)
+    cases = [
+        dict(x=xv, w=wv, transpose=False, M=2, ref=oracle.qvm(xv, *wv, N, g, bits)),
+        dict(x=xm, w=wm, transpose=True, M=32, ref=oracle.qmv(xm, *wm, g, bits)),
+    ]
+    for c in cases:
+        c["xd"] = to_dev_bf16(c["x"], dev)
+        c["wd"] = tuple(f(a, dev) for f, a in zip((to_dev_u32, to_dev_bf16, to_dev_bf16), c["w"]))
+    return cases, K, N, g, bits
+
+
+@pytest.mark.parametrize("own_workspace", (True, False))
+def test_split_k_graphs_replayed_concurrently_on_two_streams(dev, own_workspace):
+    """Two graphs captured on ONE stream, each holding a split-K call, are
+    replayed on two different streams with no synchronization between them.
+    Each must match the oracle (T2): a workspace shared between the two
+    would mix their partial sums.  With own_workspace each call gets a
+    caller-owned workspace; otherwise qmv's stream-ordered allocation is
+    captured into each graph."""
+    import torch
+
+    import bit_affine_quantized_amd as q
+    from tests.parity import check_t2
+    cases, K, N, g, bits = _split_k_cases(dev)
+    side = torch.cuda.Stream()
+    graphs = []
+    for c in cases:
+        c["y"] = torch.zeros((c["M"], N), dtype=torch.float32, device=dev)
+        ws = None
+        if own_workspace:
+            nb = q.qmv_workspace_bytes(c["M"], N, K, g, bits, c["transpose"])
+            assert nb > 0
+            ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+            c["ws"] = ws
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=side):
+            q.qmv(c["xd"], *c["wd"], transpose=c["transpose"], group_size=g, bits=bits,
+                  out_dtype=torch.float32, y=c["y"], workspace=ws)
+        graphs.append(gr)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for rep in range(5):
+        for c in cases:
+            c["y"].fill_(-1.0)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s1):
+            graphs[0].replay()
+        with torch.cuda.stream(s2):
+            graphs[1].replay()
+        with torch.cuda.stream(s1):
+            graphs[0].replay()
+        torch.cuda.synchronize()
+        for i, c in enumerate(cases):
+            check_t2(c["y"].cpu().numpy(), c["ref"], f"graph {i} replay {rep}")
+
+
+def test_with_workspace_is_bit_identical_to_qmv(dev):
+    """qmv_with_workspace and qmv run the same kernels in the same order."""
+    import torch
+
+    import bit_affine_quantized_amd as q
+    cases, K, N, g, bits = _split_k_cases(dev)
+    for c in cases:
+        y0 = q.qmv(c["xd"], *c["wd"], transpose=c["transpose"], group_size=g, bits=bits)
+        nb = q.qmv_workspace_bytes(c["M"], N, K, g, bits, c["transpose"])
+        ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+        y1 = q.qmv(c["xd"], *c["wd"], transpose=c["transpose"], group_size=g, bits=bits,
+                   workspace=ws)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(bf16_to_np_bits(y0), bf16_to_np_bits(y1))
+
+
+def test_with_workspace_too_small_raises(dev):
+    import torch
+
+    import bit_affine_quantized_amd as q
+    cases, K, N, g, bits = _split_k_cases(dev)
+    c = cases[0]
+    nb = q.qmv_workspace_bytes(c["M"], N, K, g, bits, c["transpose"])
+    ws = torch.empty(nb - 64, dtype=torch.uint8, device=dev)
+    with pytest.raises(q.QmvError, match="workspace"):
+        q.qmv(c["xd"], *c["wd"], transpose=c["transpose"], group_size=g, bits=bits, workspace=ws)
