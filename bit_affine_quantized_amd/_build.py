@@ -1,4 +1,6 @@
-"""Compile libqmv.so for gfx950 with hipcc (in-tree; no JIT cache)."""
+"""Compile libqmv.so (the matvec library) and libqmv_bench.so (measurement
+references used only by bench.py) for gfx950 with hipcc, in-tree; the two
+compile in parallel."""
 from __future__ import annotations
 
 import os
@@ -9,10 +11,11 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libqmv.so")
+BENCH_LIB = os.path.join(PKG, "libqmv_bench.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["qmv_api.hip"]
-HEADERS = ["qmv_device.h", "qmv_kernels.h", "pack_kernels.h"]
+HEADERS = ["qmv_device.h", "qmv_kernels.h", "qmv_line_kernels.h", "pack_kernels.h"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -26,16 +29,27 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _start(sources, out, verbose):
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+           *[os.path.join(CSRC, s) for s in sources], "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)
-    os.replace(tmp, LIB)
+    return subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                            text=True), tmp, out
+
+
+def build(verbose: bool = False) -> str:
+    jobs = [_start(SOURCES, LIB, verbose), _start(["bench_refs.hip"], BENCH_LIB, verbose)]
+    errors = []
+    for proc, tmp, out in jobs:
+        text = proc.communicate()[0]
+        if proc.returncode != 0:
+            errors.append(f"hipcc failed for {os.path.basename(out)}:\n{text}")
+        else:
+            os.replace(tmp, out)
+    if errors:
+        raise RuntimeError("\n".join(errors))
     return LIB
 
 

@@ -342,6 +342,20 @@ __device__ __forceinline__ bool reduce_leader(int lane) {
   return (lane & low_mask) == 0;
 }
 
+// Workgroup b of a launch runs on XCD (b mod 8): the dispatcher deals
+// workgroups to the eight XCDs in turn.  xcd_block maps the dispatch index
+// to a logical block index such that XCD x owns one contiguous run of
+// logical blocks (the x-th eighth, the first nb mod 8 XCDs one block more).
+// Kernels that give consecutive logical blocks consecutive rows then have
+// each XCD stream its own contiguous part of the weight, scales and output;
+// on MI355X this measured 4-5% faster for the one-vector matvec than the
+// dispatch order (whose neighbouring blocks sit on different XCDs).
+__device__ __forceinline__ int64_t xcd_block(int64_t b, int64_t nb) {
+  const int64_t x = b & 7, k = b >> 3;
+  const int64_t q = nb >> 3, r = nb & 7;
+  return x * q + (x < r ? x : r) + k;
+}
+
 constexpr int pow2_ceil(int v) {
   int p = 1;
   while (p < v) p <<= 1;

@@ -383,7 +383,8 @@ __global__ __launch_bounds__(WPB * kWave) void qmv_kernel(QmvArgs a) {
   // wave index, made visibly wave-uniform so row pointers live in SGPRs
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int64_t total = static_cast<int64_t>(a.nmat) * a.N;
-  const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * WPB + wid) * RPW;
+  const int64_t blk = xcd_block(blockIdx.x, gridDim.x);   // each XCD a contiguous run of rows
+  const int64_t row0 = (blk * WPB + wid) * RPW;
   const int64_t wstride = static_cast<int64_t>(Kc) * BITS;
   const int64_t gstride = Kc >> a.gshift;
 

@@ -1,0 +1,184 @@
+// One-vector quantized matvec with a straight-line body (gfx950).
+//
+// Same work split and arithmetic as qmv_kernel (qmv_kernels.h) for one x
+// vector: a workgroup of WPB waves owns RPW * WPB consecutive rows, lane l of
+// a wave takes chunks l, l + 64, ... of each of its rows, and x is staged once
+// per workgroup in LDS.  The difference is that the number of 64-lane chunk
+// steps per row, CPL, is a compile-time constant, so the kernel has no loop
+// and no data-dependent branch between its loads and their uses.  That lets
+// the compiler count the memory counter exactly.  The loads are issued in the
+// order
+//     x staging item(s), scales and biases of every step, then the weight
+//     chunks step by step (row by row within a step),
+// and since loads retire in issue order, the product of (step t, row r)
+// waits only for the chunks issued before it: a wave starts on its first
+// chunk as soon as that chunk lands instead of after its whole weight stream.
+// (The loop kernel's waits are merged over loop paths and wait for the next
+// step's loads as well.)  Row blocks follow the XCD order of xcd_block.
+//
+// Measured on MI355X for 14336x4096 4-bit g64 (graph replays over 16
+// rotated input sets, medians of interleaved rounds): loop kernel 8.01 us,
+// straight line 7.87 us, straight line with XCD row order 7.52 us.
+#pragma once
+
+#include "qmv_kernels.h"
+
+namespace qmvk {
+
+// FULL: Kc == CPL * 64 (every lane has a chunk at every step).  Otherwise
+// Kc > (CPL - 1) * 64 and lanes past Kc in the last step re-read the row's
+// last chunk and contribute zero (scale and bias term forced to 0).
+template <int BITS, int RPW, int WPB, int CPL, bool FULL>
+__global__ __launch_bounds__(WPB * kWave) void qmv_line_kernel(QmvArgs a) {
+  constexpr int NT = WPB * kWave;
+  constexpr bool PAIR = BITS <= 6;
+  constexpr int kStride = chunk_stride<PAIR, 1>();
+  constexpr int XI = (CPL * kWave + NT - 1) / NT;   // x staging items per thread
+  extern __shared__ __align__(16) unsigned char smem[];
+
+  const int Kc = a.K >> 5;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int64_t total = static_cast<int64_t>(a.nmat) * a.N;
+  const int64_t row0 = (xcd_block(blockIdx.x, gridDim.x) * WPB + wid) * RPW;
+  const int64_t wstride = static_cast<int64_t>(Kc) * BITS;
+  const int64_t gstride = Kc >> a.gshift;
+
+  const uint32_t *wrow[RPW];
+  const uint16_t *srow[RPW], *brow[RPW];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    int64_t gr = row0 + r;
+    if (gr > total - 1) gr = total - 1;
+    const bool second = gr >= a.N;
+    const int64_t lr = second ? gr - a.N : gr;
+    wrow[r] = (second ? a.mat1.w : a.mat0.w) + lr * wstride;
+    srow[r] = (second ? a.mat1.s : a.mat0.s) + lr * gstride;
+    brow[r] = (second ? a.mat1.b : a.mat0.b) + lr * gstride;
+  }
+  auto chunk_of = [&](int t) -> uint32_t {
+    return static_cast<uint32_t>(FULL ? t * kWave + lane : min(t * kWave + lane, Kc - 1));
+  };
+
+  // ---- 1. raw x of this thread's staging item(s)
+  uint32_t raw[XI][16];
+#pragma unroll
+  for (int i = 0; i < XI; ++i) {
+    const int it = min(static_cast<int>(threadIdx.x) + i * NT, Kc - 1);
+    load_x_chunk(byte_offset(a.x, static_cast<uint32_t>(it) * 64), raw[i]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- 2. scales and biases of every step
+  uint16_t sv[CPL][RPW], bv[CPL][RPW];
+#pragma unroll
+  for (int t = 0; t < CPL; ++t) {
+    const uint32_t gi = chunk_of(t) >> a.gshift;
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      sv[t][r] = *byte_offset(srow[r], gi * 2);
+      bv[t][r] = *byte_offset(brow[r], gi * 2);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- 3. the weight chunks, in a fixed issue order (the waits follow it)
+  uint32_t w[CPL][RPW][BITS];
+#pragma unroll
+  for (int t = 0; t < CPL; ++t) {
+    const uint32_t c = chunk_of(t);
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      load_chunk<BITS>(byte_offset(wrow[r], c * (BITS * 4)), w[t][r]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // ---- 4. x into LDS (waits for x only), one barrier
+#pragma unroll
+  for (int i = 0; i < XI; ++i) {
+    const int it = static_cast<int>(threadIdx.x) + i * NT;
+    if ((i + 1) * NT <= CPL * kWave || it < Kc) {
+      const int its = min(it, Kc - 1);
+      if constexpr (PAIR) stage_pairs_raw<BITS, 1>(raw[i], smem, 0, its);
+      else stage_f32_raw<1>(raw[i], smem, 0, its);
+    }
+  }
+  __syncthreads();
+
+  // ---- 5. products, one step at a time
+  const PairConsts pk = pair_consts<BITS>();
+  float acc[RPW], accz[RPW];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) acc[r] = accz[r] = 0.0f;
+#pragma unroll
+  for (int t = 0; t < CPL; ++t) {
+    const bool live = FULL || (t + 1) * kWave <= Kc || t * kWave + lane < Kc;
+    const unsigned char *chunk = smem + chunk_of(t) * kStride;
+    const float xs = *reinterpret_cast<const float *>(chunk + vec_bytes<PAIR>());
+    if constexpr (PAIR) {
+      uint32_t xp[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(chunk + q * 16);
+        xp[4 * q] = v.x; xp[4 * q + 1] = v.y; xp[4 * q + 2] = v.z; xp[4 * q + 3] = v.w;
+      }
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        float d = 0.0f;
+        static_for<0, 16>([&](auto i) {
+          constexpr int I = decltype(i)::value;
+          d = dot2_bf16(make_pair<BITS, I>(w[t][r], pk), xp[I], d);
+        });
+        float s = bf16_to_f32(sv[t][r]);
+        float zc = fmaf(-static_cast<float>(1 << BITS), s, bf16_to_f32(bv[t][r]));   // z - 2^b s
+        if (!live) s = zc = 0.0f;
+        acc[r] = fmaf(s, d, acc[r]);
+        accz[r] = fmaf(zc, xs, accz[r]);
+      }
+    } else {
+      float xf[32];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float4 v = *reinterpret_cast<const float4 *>(chunk + q * 16);
+        xf[4 * q] = v.x; xf[4 * q + 1] = v.y; xf[4 * q + 2] = v.z; xf[4 * q + 3] = v.w;
+      }
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        float d0 = 0.0f, d1 = 0.0f;
+        static_for<0, 16>([&](auto h) {
+          constexpr int k = 2 * decltype(h)::value;
+          d0 = fmaf(code_f32<BITS, k>(w[t][r]), xf[k], d0);
+          d1 = fmaf(code_f32<BITS, k + 1>(w[t][r]), xf[k + 1], d1);
+        });
+        float s = bf16_to_f32(sv[t][r]);
+        float z = bf16_to_f32(bv[t][r]);
+        if (!live) s = z = 0.0f;
+        acc[r] = fmaf(s, d0 + d1, fmaf(z, xs, acc[r]));
+      }
+    }
+  }
+
+  // ---- 6. reduce across the wave and store (one bf16 rounding)
+  constexpr int V = pow2_ceil(RPW);
+  float vals[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) vals[i] = 0.0f;
+#pragma unroll
+  for (int r = 0; r < RPW; ++r)
+    vals[r] = PAIR ? fmaf(acc[r], 1.0f / static_cast<float>(1 << PairPlan<BITS>::P), accz[r]) : acc[r];
+  const float tot = wave_reduce_many<V>(vals, lane);
+  if (reduce_leader<V>(lane)) {
+    const int r = reduce_index<V>(lane);
+    const int64_t gr = row0 + r;
+    if (r < RPW && gr < total) {
+      const bool second = gr >= a.N;
+      const int64_t lr = second ? gr - a.N : gr;
+      void *y = second ? a.mat1.y : a.mat0.y;
+      if (a.out_f32) static_cast<float *>(y)[lr] = tot;
+      else static_cast<uint16_t *>(y)[lr] = f32_to_bf16(tot);
+    }
+  }
+}
+
+}  // namespace qmvk
