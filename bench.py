@@ -9,10 +9,12 @@ One step = one call of the workload's entry point(s) on one set of
 device-resident inputs (for the FFN step: the gate/up launch and the fused
 down-projection launch).  Steps rotate over enough distinct copies of the
 inputs (>= 512 MB in total) that the 256 MB last-level cache cannot serve a
-repeat.  The K timed steps are captured into one HIP graph and replayed, so
-the host's per-launch cost (several microseconds through Python) does not
-starve the GPU; time is taken with HIP events on the replay stream.  The
-eager (host-launched) time per step is reported beside it.  Bytes are
+repeat.  The K timed steps are launched eagerly behind a bounded device spin that
+holds the stream while the host enqueues them, so the timed region (HIP
+events on the stream) holds only the K launches back to back: neither the
+host's per-launch cost (several microseconds through Python) nor a graph
+launch falls inside it.  The time of one HIP-graph replay of the K steps and
+the unqueued eager time are reported beside it.  Bytes are
 algorithmic: packed weights, bf16 scales and biases, activations and
 outputs, each counted once per step.
 
@@ -20,6 +22,8 @@ Other modes (profiling aids):
   --no-cpu-baseline   skip the CPU oracle timing
   --copy-calibration  run a plain 256 MiB device copy (counter scaling)
   --copy-reference    time a plain device copy of the workload's byte count
+  --read-reference    time the streaming-read reference (libqmv_bench.so) at
+                      the workload's byte count, alone and with y's stores
   --eager             time host-launched steps instead of a graph replay
 """
 from __future__ import annotations
@@ -41,8 +45,8 @@ METRIC = "qmv GB/s & % of HBM peak, 4-bit g64 N=14336 K=4096 batch 1"
 HBM_PEAK_GBS = 8000.0
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [os.path.join(ROOT, "bit_affine_quantized_amd", "csrc", f)
-                  for f in ("qmv_device.h", "qmv_kernels.h", "qmv_api.hip", "pack_kernels.h",
-                            "qvm_kernels.h", "qmm_kernels.h")]
+                  for f in ("qmv_device.h", "qmv_kernels.h", "qmv_line_kernels.h", "qmv_api.hip",
+                            "pack_kernels.h", "qvm_kernels.h", "qmm_kernels.h")]
 ROTATE_BYTES = 512e6
 
 
@@ -100,22 +104,32 @@ def make_qmv(N, K, bits, g, M, name):
         del w
         x = _dev_bf16(torch, synth.activation_bf16((M, K)), dev)
         sets = max(2, math.ceil(ROTATE_BYTES / nbytes))
+        # split-K calls (5 or more rows of x) get a caller-owned workspace
+        nws = q.qmv_workspace_bytes(M, N, K, g, bits, True)
         bufs = [(x.clone(), w_q.clone(), s.clone(), b.clone(),
-                 torch.empty((M, N), dtype=torch.bfloat16, device=dev))
+                 torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+                 torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None)
                 for _ in range(sets)]
 
         def step(i, stream):
-            xb, wb, sb, bb, yb = bufs[i % sets]
-            q.qmv(xb, wb, sb, bb, group_size=g, bits=bits, y=yb, stream=stream)
+            xb, wb, sb, bb, yb, ws = bufs[i % sets]
+            q.qmv(xb, wb, sb, bb, group_size=g, bits=bits, y=yb, stream=stream,
+                  workspace=ws)
         return step, sets
 
-    def cpu(budget_s):
+    def cpu():
         import oracle
         import synth
         w_q, s, b = oracle.quantize_pack(synth.weight((N, K)), g, bits)
         x = synth.activation_bf16((M, K))
-        return lambda: oracle.qmv(x, w_q, s, b, g, bits), \
-            f"full {N}x{K} b{bits} g{g} M={M} qmv"
+
+        def blocks(T):
+            edges = [N * i // T for i in range(T + 1)]
+            return [(lambda r0=r0, r1=r1: oracle.qmv(
+                x, w_q[r0:r1], s[r0:r1], b[r0:r1], g, bits))
+                for r0, r1 in zip(edges[:-1], edges[1:]) if r1 > r0]
+        return (lambda: oracle.qmv(x, w_q, s, b, g, bits),
+                f"{N}x{K} b{bits} g{g} M={M} qmv", blocks)
     return Workload(name, nbytes, setup, 1, cpu)
 
 
@@ -134,23 +148,32 @@ def make_qvm(K, N, bits, g, M, name):
         del w
         x = _dev_bf16(torch, synth.activation_bf16((M, K)), dev)
         sets = max(2, math.ceil(ROTATE_BYTES / nbytes))
+        nws = q.qmv_workspace_bytes(M, N, K, g, bits, False)
         bufs = [(x.clone(), w_q.clone(), s.clone(), b.clone(),
-                 torch.empty((M, N), dtype=torch.bfloat16, device=dev))
+                 torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+                 torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None)
                 for _ in range(sets)]
 
         def step(i, stream):
-            xb, wb, sb, bb, yb = bufs[i % sets]
+            xb, wb, sb, bb, yb, ws = bufs[i % sets]
             q.qmv(xb, wb, sb, bb, transpose=False, group_size=g, bits=bits,
-                  y=yb, stream=stream)
+                  y=yb, stream=stream, workspace=ws)
         return step, sets
 
-    def cpu(budget_s):
+    def cpu():
         import oracle
         import synth
         w_q, s, b = oracle.quantize_pack(synth.weight((K, N)), g, bits)
         x = synth.activation_bf16((M, K))
-        return lambda: oracle.qvm(x, w_q, s, b, N, g, bits), \
-            f"full {K}x{N} b{bits} g{g} M={M} qvm"
+
+        def blocks(T):
+            # K-row blocks give partial products; the split is summed after
+            edges = [K * i // T for i in range(T + 1)]
+            return [(lambda r0=r0, r1=r1: oracle.qvm(
+                x[:, r0:r1], w_q[r0:r1], s[r0:r1], b[r0:r1], N, g, bits))
+                for r0, r1 in zip(edges[:-1], edges[1:]) if r1 > r0]
+        return (lambda: oracle.qvm(x, w_q, s, b, N, g, bits),
+                f"{K}x{N} b{bits} g{g} M={M} qvm", blocks)
     return Workload(name, nbytes, setup, 1, cpu)
 
 
@@ -176,12 +199,18 @@ def make_dequant(N, K, bits, g, name):
             q.qmv_dequantize(wb, sb, bb, g, bits, out=ob, stream=stream)
         return step, sets
 
-    def cpu(budget_s):
+    def cpu():
         import oracle
         import synth
         w_q, s, b = oracle.quantize_pack(synth.weight((N, K)), g, bits)
-        return lambda: oracle.dequantize(w_q, s, b, K, g, bits), \
-            f"full {N}x{K} b{bits} g{g} dequantize"
+
+        def blocks(T):
+            edges = [N * i // T for i in range(T + 1)]
+            return [(lambda r0=r0, r1=r1: oracle.dequantize(
+                w_q[r0:r1], s[r0:r1], b[r0:r1], K, g, bits))
+                for r0, r1 in zip(edges[:-1], edges[1:]) if r1 > r0]
+        return (lambda: oracle.dequantize(w_q, s, b, K, g, bits),
+                f"{N}x{K} b{bits} g{g} dequantize", blocks)
     return Workload(name, nbytes, setup, 1, cpu)
 
 
@@ -359,20 +388,101 @@ def workloads():
     return W
 
 
-def cpu_baseline(wl: Workload, budget_s=10.0):
-    fn, what = wl.oracle_fn(budget_s)
-    reps, t0 = 0, time.perf_counter()
-    while True:
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_threads() -> int:
+    """Threads for the multi-threaded oracle run: the CPUs this process may
+    run on, capped by OMP_NUM_THREADS when the environment sets it (a shared
+    host gives each GPU a share of its cores)."""
+    t = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        t = min(t, int(cap))
+    return max(1, t)
+
+
+def _median_seconds(fn, runs):
+    ts = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
         fn()
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    per = el / reps
-    return {"value": round(wl.nbytes / per / 1e9, 4), "unit": "GB/s",
-            "cores": 1, "kind": "oracle",
-            "sample": f"{what}, {reps} runs in {el:.1f} s (plain C, fp64 "
-                      "dequant-and-dot, 1 thread)"}
+        ts.append(time.perf_counter() - t0)
+    ts.sort()
+    return ts[len(ts) // 2], ts
+
+
+def cpu_baseline(wl: Workload, runs: int = 5):
+    """The oracle (plain C, fp64 dequant-and-dot, untuned) on the workload's
+    full inputs: median of `runs` runs at 1 thread and at T threads.  The T
+    threads take contiguous row blocks of W, each calling the oracle on its
+    block (ctypes releases the interpreter lock during the call)."""
+    from concurrent.futures import ThreadPoolExecutor
+    one, what, rows_fn = wl.oracle_fn()
+    T = cpu_threads()
+    t1, all1 = _median_seconds(one, runs)
+    pool = ThreadPoolExecutor(max_workers=T)
+    try:
+        blocks = rows_fn(T)
+
+        def many():
+            list(pool.map(lambda f: f(), blocks))
+        many()                                  # warm the pool
+        tT, allT = _median_seconds(many, runs)
+    finally:
+        pool.shutdown()
+    return {"value": round(wl.nbytes / tT / 1e9, 4), "unit": "GB/s",
+            "cores": T, "kind": "oracle",
+            "value_1_thread": round(wl.nbytes / t1 / 1e9, 4),
+            "median_s": {"1": round(t1, 4), str(T): round(tT, 4)},
+            "runs": runs, "cpu_model": cpu_model(),
+            "affinity_cpus": len(os.sched_getaffinity(0)),
+            "sample": f"{what}: the whole workload, median of {runs} runs at "
+                      f"1 and at {T} threads (row blocks); plain C oracle, "
+                      "fp64 dequant-and-dot"}
+
+
+def _time_queued(step, steps, stream, info=None):
+    """K eager launches queued behind a bounded device spin, timed by events.
+
+    The spin (a few times the measured host enqueue time of the K steps)
+    holds the stream while the host enqueues the start event, the K steps and
+    the end event, so the timed region holds only the K launches running back
+    to back; neither the host's per-launch cost nor a graph launch falls
+    inside it.  If the host took longer than the spin to enqueue, the queue
+    may have drained and the time is pessimistic; `queue_drained` says so."""
+    import torch
+    torch.cuda.synchronize()
+    probe = min(steps, 20)
+    h0 = time.perf_counter()
+    for i in range(probe):
+        step(i, stream)
+    host_per_step = (time.perf_counter() - h0) / probe
+    torch.cuda.synchronize()
+    spin_ms = min(max(1.0, 3e3 * host_per_step * steps), 3000.0)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int(spin_ms * _spin_cycles_per_ms()))
+    h0 = time.perf_counter()
+    t0.record(stream)
+    for i in range(steps):
+        step(i, stream)
+    t1.record(stream)
+    enqueue_ms = (time.perf_counter() - h0) * 1e3
+    torch.cuda.synchronize()
+    if info is not None:
+        info["spin_ms"] = round(spin_ms, 3)
+        info["host_enqueue_ms"] = round(enqueue_ms, 3)
+        info["queue_drained"] = enqueue_ms > spin_ms
+    return t0.elapsed_time(t1) / steps
 
 
 def _time_eager(step, steps, stream):
@@ -387,9 +497,36 @@ def _time_eager(step, steps, stream):
     return t0.elapsed_time(t1) / steps
 
 
-def _time_graph(step, steps, warmup):
+_SPIN_CYCLES_PER_MS = None
+
+
+def _spin_cycles_per_ms():
+    """Cycles of torch's device sleep kernel per millisecond on this GPU."""
+    global _SPIN_CYCLES_PER_MS
+    if _SPIN_CYCLES_PER_MS is None:
+        import torch
+        st = torch.cuda.current_stream()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(1000)
+        e0.record(st)
+        torch.cuda._sleep(2_000_000)
+        e1.record(st)
+        torch.cuda.synchronize()
+        _SPIN_CYCLES_PER_MS = 2_000_000 / max(e0.elapsed_time(e1), 1e-3)
+    return _SPIN_CYCLES_PER_MS
+
+
+def _time_graph(step, steps, warmup, info=None):
     """Capture `steps` steps into one HIP graph and time a replay: the GPU
-    runs the launches back to back with no host launch cost in between."""
+    runs the launches back to back with no host launch cost in between.
+
+    The start event would otherwise be reached while the host is still
+    submitting the graph, and that submission latency would count as kernel
+    time.  So a bounded device spin (a few times the measured submission
+    time) is queued first: the start event, the replay and the end event are
+    all enqueued while the GPU spins, and the timed region holds only the
+    replayed launches."""
     import torch
     side = torch.cuda.Stream()
     with torch.cuda.stream(side):        # per-stream set-up happens outside capture
@@ -402,15 +539,23 @@ def _time_graph(step, steps, warmup):
             step(i, cs)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    graph.replay()                       # warm replay
+    h0 = time.perf_counter()
+    graph.replay()                       # warm replay; its host submission time sizes the spin
+    h1 = time.perf_counter()
     torch.cuda.synchronize()
+    submit_ms = (h1 - h0) * 1e3
+    spin_ms = min(max(1.0, 4.0 * submit_ms), 200.0)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int(spin_ms * _spin_cycles_per_ms()))
     t0.record(stream)
     graph.replay()
     t1.record(stream)
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / steps
+    if info is not None:
+        info["graph_host_submit_ms"] = round(submit_ms, 3)
+        info["graph_spin_ms"] = round(spin_ms, 3)
     del graph
     return ms
 
@@ -426,7 +571,10 @@ def run_workload(wl: Workload, steps: int, warmup: int, want_cpu: bool,
         step(i, stream)
     torch.cuda.synchronize()
     ms_eager = _time_eager(step, steps, stream)
-    ms = _time_graph(step, steps, warmup) if use_graph else ms_eager
+    qinfo, ginfo = {}, {}
+    ms_queued = _time_queued(step, steps, stream, qinfo)
+    ms_graph = _time_graph(step, steps, warmup, ginfo) if use_graph else None
+    ms = ms_queued
     gbs = wl.nbytes / (ms * 1e-3) / 1e9
     res = {
         "metric": METRIC if wl.name.startswith("qmv_14336x4096_b4_g64_m1")
@@ -438,8 +586,11 @@ def run_workload(wl: Workload, steps: int, warmup: int, want_cpu: bool,
         "config": {"workload": wl.name, "bytes_per_step": wl.nbytes,
                    "launches_per_step": wl.launches,
                    "input_sets_rotated": sets,
-                   "timing": "hip_graph_replay" if use_graph else "eager",
-                   "eager_ms_per_step": round(ms_eager, 6),
+                   "timing": "eager launches queued behind a device spin, HIP events",
+                   **qinfo,
+                   "graph_ms_per_step": None if ms_graph is None else round(ms_graph, 6),
+                   **ginfo,
+                   "unqueued_eager_ms_per_step": round(ms_eager, 6),
                    "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)},
     }
     res["roofline"] = {"bound": "hbm", "achieved": round(gbs, 2),
@@ -490,6 +641,49 @@ def copy_reference(nbytes: int, steps: int):
             "frac_of_8TBs": round(2 * n / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def read_reference(nbytes: int, rows: int, steps: int):
+    """The streaming-read reference (libqmv_bench.so, qmv_bench_read) over
+    `nbytes` bytes, rotated over >= 512 MB and timed like the workloads:
+    alone, and writing one bf16 per row-sized span as a matvec writes y."""
+    import ctypes
+    import torch
+    from bit_affine_quantized_amd import _build
+    L = ctypes.CDLL(_build.BENCH_LIB)
+    L.qmv_bench_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
+                                 ctypes.c_uint64, ctypes.c_void_p]
+    L.qmv_bench_read.restype = ctypes.c_int
+    n = (nbytes // 16) * 16
+    every = max(16, (n // rows) // 16 * 16)
+    sets = max(2, math.ceil(ROTATE_BYTES / n))
+    bufs = [(torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda"),
+             torch.empty(n // every + 1, dtype=torch.int16, device="cuda"))
+            for _ in range(sets)]
+    torch.cuda.synchronize()
+    out = {"read_bytes": n, "input_sets_rotated": sets}
+    for label, store in (("read", 0), ("read_and_store", every)):
+        def step(i, stream, store=store):
+            a, y = bufs[i % sets]
+            rc = L.qmv_bench_read(ctypes.c_void_p(a.data_ptr()), n,
+                                  ctypes.c_void_p(y.data_ptr()), store,
+                                  ctypes.c_void_p(stream.cuda_stream))
+            if rc:
+                raise RuntimeError(f"qmv_bench_read failed: {rc}")
+        stream = torch.cuda.current_stream()
+        for i in range(20):
+            step(i, stream)
+        info = {}
+        ms = _time_queued(step, steps, stream, info)
+        ms_graph = _time_graph(step, steps, 0)
+        out[label] = {"ms_per_launch": round(ms, 6),
+                      "GBs": round(n / (ms * 1e-3) / 1e9, 1),
+                      "frac_of_8TBs": round(n / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                      "graph_ms_per_launch": round(ms_graph, 6),
+                      "queue_drained": info.get("queue_drained")}
+        if store:
+            out[label]["outputs"] = n // every
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -502,6 +696,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--copy-reference", action="store_true",
                     help="time a plain device copy of the workload's size")
+    ap.add_argument("--read-reference", action="store_true",
+                    help="time the streaming-read reference at the workload's byte count")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches instead of a graph replay")
     args = ap.parse_args()
@@ -524,6 +720,12 @@ def main():
     if args.copy_reference:
         n = args.workload or synth.HEADLINE["name"]
         print(json.dumps({"workload": n, **copy_reference(W[n].nbytes,
+                                                          args.steps)}))
+        return
+    if args.read_reference:
+        n = args.workload or synth.HEADLINE["name"]
+        rows = synth.HEADLINE["N"] if n == synth.HEADLINE["name"] else 4096
+        print(json.dumps({"workload": n, **read_reference(W[n].nbytes, rows,
                                                           args.steps)}))
         return
     names = list(W) if args.all else [args.workload or synth.HEADLINE["name"]]
