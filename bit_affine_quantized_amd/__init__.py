@@ -36,6 +36,7 @@ SIGNATURES = {
     "qmv_pack": [_P, _I64, _I64, _I, _I, _P, _P, _P, _P],
     "qmv": [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _I, _I, _I, _P],
     "qmv_workspace_bytes": [_I64, _I64, _I64, _I, _I, _I, _P],
+    "qmv_noalloc": [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _I, _I, _I, _P],
     "qmv_with_workspace": [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _I, _I, _I,
                            _P, ctypes.c_size_t, _P],
     "qmv_gate_up": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I, _I, _P],

@@ -5,6 +5,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "qmv.h"
@@ -683,6 +684,36 @@ int qmv_impl(const uint16_t *x, const uint32_t *w_q, const uint16_t *scales, con
   return ok();
 }
 
+// ------------------------------------------------------------------ no-alloc scratch
+// qmv_noalloc's workspace: a static device array, one copy per GPU, held from
+// the module's load until the process ends.  In host code `scratch` only
+// names the symbol; its device address on each GPU comes from
+// hipGetSymbolAddress, taken once per device (with that device current) on
+// the entry point's first call there, and only that address is used.
+constexpr size_t kScratchBytes = size_t(16) << 20;   // 16 MiB
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void *g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+int scratch_of_current_device(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(QMV_EHIP, "qmv_noalloc: hipGetDevice failed");
+  if (dev < 0 || dev >= kMaxDevices) return fail(QMV_EUNSUPPORTED, "qmv_noalloc: device %d out of range", dev);
+  std::call_once(g_scratch_once[dev], [dev] {
+    void *p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = p;
+  });
+  if (g_scratch_err[dev] != hipSuccess || g_scratch_ptr[dev] == nullptr)
+    return fail(QMV_EHIP, "qmv_noalloc: hipGetSymbolAddress of the scratch array failed on device %d: %s",
+                dev, hipGetErrorString(g_scratch_err[dev]));
+  *out = g_scratch_ptr[dev];
+  return QMV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -710,6 +741,25 @@ int qmv_with_workspace(const uint16_t *x, const uint32_t *w_q, const uint16_t *s
   ws.bytes = workspace ? workspace_bytes : 0;
   return qmv_impl(x, w_q, scales, biases, y, M, N, K, group_size, bits, transpose, out_dtype, ws,
                   static_cast<hipStream_t>(stream));
+}
+
+int qmv_noalloc(const uint16_t *x, const uint32_t *w_q, const uint16_t *scales, const uint16_t *biases,
+                void *y, int64_t M, int64_t N, int64_t K, int group_size, int bits, int transpose,
+                int out_dtype, void *stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Ws sizing;
+  sizing.sizing = true;
+  if (int rc = qmv_impl(x, w_q, scales, biases, y, M, N, K, group_size, bits, transpose, out_dtype, sizing, st))
+    return rc;
+  if (sizing.need > kScratchBytes)
+    return fail(QMV_EINVAL, "qmv_noalloc: this call needs a %zu-byte workspace; the scratch array holds %zu "
+                "bytes (qmv_with_workspace takes a larger one)", sizing.need, kScratchBytes);
+  Ws ws;
+  if (sizing.need > 0) {
+    if (int rc = scratch_of_current_device(&ws.ptr)) return rc;
+    ws.bytes = kScratchBytes;
+  }
+  return qmv_impl(x, w_q, scales, biases, y, M, N, K, group_size, bits, transpose, out_dtype, ws, st);
 }
 
 int qmv(const uint16_t *x, const uint32_t *w_q, const uint16_t *scales, const uint16_t *biases,

@@ -129,6 +129,24 @@ int qmv_with_workspace(const uint16_t *x, const uint32_t *w_q,
                        void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * qmv_noalloc -- qmv for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): same arguments and bit-identical results as qmv, but the
+ * split-K partial sums go to a static device array of 16 MiB that the
+ * library holds on each GPU it runs on until the process ends; no
+ * allocation, no free.  A call that needs more than 16 MiB
+ * (qmv_workspace_bytes) returns QMV_EINVAL before any HIP call.  Every call
+ * on one GPU shares that GPU's array: calls that may overlap on one GPU
+ * (different streams, graphs replayed concurrently) race and must be
+ * serialized by the caller.  The array needs no clearing between calls
+ * (every slice writes its partial sums before they are read).
+ */
+int qmv_noalloc(const uint16_t *x, const uint32_t *w_q, const uint16_t *scales,
+                const uint16_t *biases, void *y, int64_t M, int64_t N,
+                int64_t K, int group_size, int bits, int transpose,
+                int out_dtype, void *stream);
+
+/*
  * qmv_gate_up -- dual-output matvec over one input in ONE launch
  * (metrale QuantWeights::gemv_gate_up_with, whose default is two gemv calls;
  * the MlxInt8Weight implementation uses a single launch).

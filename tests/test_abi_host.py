@@ -191,3 +191,14 @@ def test_with_workspace_too_small_is_rejected_before_any_launch():
     rc = L.qmv_with_workspace(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4096, 4096, 64, 4,
                               0, 0, ctypes.c_void_p(0x1008), need, None)
     assert rc == q.QMV_EINVAL and b"aligned" in L.qmv_last_error()
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch():
+    """qmv_noalloc's static scratch holds 16 MiB; a larger split-K call is
+    refused before any HIP call."""
+    rc, need = _ws_bytes(3, 65536, 65536, transpose=0)
+    assert rc == q.QMV_OK and need > 16 << 20
+    L = q.lib()
+    rc = L.qmv_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, 3, 65536, 65536, 64, 4, 0, 0, None)
+    assert rc == q.QMV_EINVAL
+    assert b"scratch" in L.qmv_last_error()
