@@ -82,9 +82,10 @@ def read_traffic(workload: str, src_hash: str):
 class Workload:
     """name, algorithmic bytes per step, and setup(dev) -> (step(i), check)."""
 
-    def __init__(self, name, nbytes, setup, launches=1, oracle_fn=None):
+    def __init__(self, name, nbytes, setup, launches=1, oracle_fn=None, dtype="bf16"):
         self.name, self.nbytes, self.setup = name, nbytes, setup
         self.launches, self.oracle_fn = launches, oracle_fn
+        self.dtype = dtype
 
 
 def _dev_bf16(torch, a, dev):
@@ -212,6 +213,30 @@ def make_dequant(N, K, bits, g, name):
         return (lambda: oracle.dequantize(w_q, s, b, K, g, bits),
                 f"{N}x{K} b{bits} g{g} dequantize", blocks)
     return Workload(name, nbytes, setup, 1, cpu)
+
+
+def make_pack(N, K, bits, g, name):
+    """Device quantize + pack of an fp32 [N, K] weight: reads 4 bytes per
+    weight, writes the packed codes, scales and biases."""
+    nbytes = 4 * N * K + qbytes(N, K, bits, g)
+
+    def setup(dev):
+        import torch
+        import bit_affine_quantized_amd as q
+        import synth
+        w = torch.from_numpy(synth.weight((N, K))).to(dev)
+        sets = max(2, math.ceil(ROTATE_BYTES / nbytes))
+        bufs = [(w.clone(), torch.empty((N, K * bits // 32), dtype=torch.int32, device=dev),
+                 torch.empty((N, K // g), dtype=torch.bfloat16, device=dev),
+                 torch.empty((N, K // g), dtype=torch.bfloat16, device=dev))
+                for _ in range(sets)]
+        del w
+
+        def step(i, stream):
+            wb, wq, sb, bb = bufs[i % sets]
+            q.qmv_pack(wb, g, bits, stream=stream, out=(wq, sb, bb))
+        return step, sets
+    return Workload(name, nbytes, setup, 1, dtype="f32")
 
 
 def make_gate_up(N, K, bits, g, name):
@@ -376,6 +401,7 @@ def workloads():
         W[n] = make_qvm(4096, 4096, 4, 64, M, n)
     W["dequant_14336x4096_b4_g64"] = make_dequant(14336, 4096, 4, 64,
                                                   "dequant_14336x4096_b4_g64")
+    W["pack_14336x4096_b4_g64"] = make_pack(14336, 4096, 4, 64, "pack_14336x4096_b4_g64")
     m = synth.MOE
     for srt in (False, True):
         n = f"moe_gather_64x2048x2048_b4_g64_t16_top8_{'sorted' if srt else 'unsorted'}"
@@ -582,7 +608,7 @@ def run_workload(wl: Workload, steps: int, warmup: int, want_cpu: bool,
         "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps,
         "warmup": warmup, "ms_per_step": round(ms, 6),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic",
+        "dtype": wl.dtype, "data": "synthetic",
         "config": {"workload": wl.name, "bytes_per_step": wl.nbytes,
                    "launches_per_step": wl.launches,
                    "input_sets_rotated": sets,

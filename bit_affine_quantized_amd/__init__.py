@@ -128,9 +128,10 @@ def _out_code(out_dtype):
 
 
 # ----------------------------------------------------------------- API
-def qmv_pack(w, group_size: int = 64, bits: int = 4, stream=None):
+def qmv_pack(w, group_size: int = 64, bits: int = 4, stream=None, out=None):
     """Quantize fp32 W [N, K] on the device -> (w_q uint32-as-int32 [N,
-    K*bits/32], scales bf16 [N, K/g], biases bf16 [N, K/g])."""
+    K*bits/32], scales bf16 [N, K/g], biases bf16 [N, K/g]).  ``out`` may
+    give the three output tensors."""
     torch = _torch()
     _need(w, torch.float32, "w")
     if w.dim() != 2:
@@ -138,9 +139,17 @@ def qmv_pack(w, group_size: int = 64, bits: int = 4, stream=None):
     N, K = w.shape
     words = (K * bits) // 32 if bits > 0 else 0
     groups = K // group_size if group_size > 0 else 0
-    w_q = torch.empty((N, max(words, 1)), dtype=torch.int32, device=w.device)
-    s = torch.empty((N, max(groups, 1)), dtype=torch.bfloat16, device=w.device)
-    b = torch.empty_like(s)
+    if out is None:
+        w_q = torch.empty((N, max(words, 1)), dtype=torch.int32, device=w.device)
+        s = torch.empty((N, max(groups, 1)), dtype=torch.bfloat16, device=w.device)
+        b = torch.empty_like(s)
+    else:
+        w_q, s, b = out
+        _wq(w_q)
+        _bits16(s, "scales")
+        _bits16(b, "biases")
+        if w_q.numel() < N * words or s.numel() < N * groups or b.numel() < N * groups:
+            raise ValueError("qmv_pack: output tensors too small")
     _call("qmv_pack", _ptr(w), N, K, group_size, bits, _ptr(w_q), _ptr(s),
           _ptr(b), _stream(stream))
     return w_q, s, b

@@ -7,31 +7,76 @@
 
 namespace qmvk {
 
-// One thread per group of g consecutive K-elements (mlx-cpu 0.30.1
-// quantized.h, affine_quantize).  Every step is one IEEE fp32 operation:
-// the library is built without FMA contraction and with correctly rounded
-// division, and roundf rounds half away from zero, so the codes and the bf16
-// scale/bias bits are fully determined by the input.
-__global__ __launch_bounds__(256) void pack_kernel(const float *__restrict__ w, int64_t N, int64_t K,
-                                                   int g, int bits, uint32_t *__restrict__ w_q,
-                                                   uint16_t *__restrict__ scales,
-                                                   uint16_t *__restrict__ biases) {
-  const int64_t groups = K / g;
-  const int64_t gi = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (gi >= N * groups) return;
-  const int64_t n = gi / groups;
-  const int64_t j = gi - n * groups;
-  const float *src = w + n * K + j * g;
+// Quantize and pack (mlx-cpu 0.30.1 quantized.h, affine_quantize).
+//
+// A group of g consecutive values is spread over g/4 adjacent lanes, four
+// values per lane, as the page's quantizer spreads a group over a SIMD
+// group: one 16-byte load per lane, and since groups are consecutive in
+// memory (row-major W, K a multiple of g) a wave's loads are one contiguous
+// 1 KB run.  w_min and w_max are reduced across the group's lanes (min and
+// max are exact, so the reduction order cannot change them; the sign of a
+// zero minimum or maximum never reaches the scale, bias or codes), every
+// lane then runs the page's scale and bias steps, and each lane quantizes
+// its four values.  Every step is one IEEE fp32 operation: the library is
+// built without FMA contraction and with correctly rounded division, and
+// roundf rounds half away from zero, so codes and bf16 scale/bias bits are
+// fully determined by the input.  A lane's four codes form one 4b-bit field
+// at bit 4b*u of its group's bit stream; the fields are OR-ed into the
+// workgroup's words in LDS (at most two words per lane; OR is order
+// independent) and the words are then written out contiguously.
+// (One thread per group, reading its group straight from memory: 1.74 ms for
+// a 14336x4096 pack on MI355X; one thread per group staged through LDS:
+// 126 us.)
+constexpr int kPackThreads = 256;
+
+template <int G>
+struct PackShape {
+  static constexpr int LPG = G / 4;                  // lanes per group
+  static constexpr int GPB = kPackThreads / LPG;     // groups per workgroup
+  static constexpr int MAX_WORDS = GPB * G * 8 / 32; // LDS words for 8-bit codes
+};
+
+template <int LPG>
+__device__ __forceinline__ float group_reduce(float v, bool is_min) {
+#pragma unroll
+  for (int off = 1; off < LPG; off <<= 1) {
+    const float o = __shfl_xor(v, off, 64);
+    v = is_min ? (o < v ? o : v) : (o > v ? o : v);
+  }
+  return v;
+}
+
+template <int G>
+__global__ __launch_bounds__(kPackThreads) void pack_kernel(const float *__restrict__ w, int64_t ngroups,
+                                                            int bits, uint32_t *__restrict__ w_q,
+                                                            uint16_t *__restrict__ scales,
+                                                            uint16_t *__restrict__ biases) {
+  using S = PackShape<G>;
+  __shared__ uint32_t words[S::MAX_WORDS];
+  const int wpg = G * bits / 32;                     // words per group
+  const int64_t g0 = static_cast<int64_t>(blockIdx.x) * S::GPB;
+  const int gl = threadIdx.x / S::LPG, u = threadIdx.x % S::LPG;
+  const int64_t gi = g0 + gl;
+  const bool live = gi < ngroups;
+
+  for (int i = threadIdx.x; i < S::GPB * wpg; i += kPackThreads) words[i] = 0u;
+
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  f32x4_t v = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (live) v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(w + gi * G) + u);   // read once
+
+  float w_min = FLT_MAX;
+  float w_max = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    w_min = v[e] < w_min ? v[e] : w_min;
+    w_max = v[e] > w_max ? v[e] : w_max;
+  }
+  w_min = group_reduce<S::LPG>(w_min, true);
+  w_max = group_reduce<S::LPG>(w_max, false);
 
   const float n_bins = static_cast<float>((1 << bits) - 1);
   const float eps = 1e-7f;
-  float w_min = FLT_MAX;
-  float w_max = 0.0f;
-  for (int i = 0; i < g; ++i) {
-    const float v = src[i];
-    w_min = v < w_min ? v : w_min;
-    w_max = v > w_max ? v : w_max;
-  }
   float scale = (w_max - w_min) / n_bins;
   scale = scale < eps ? eps : scale;
   const bool side = fabsf(w_min) > fabsf(w_max);
@@ -43,26 +88,29 @@ __global__ __launch_bounds__(256) void pack_kernel(const float *__restrict__ w, 
     scale = edge / q0;
     bias = edge;
   }
-  scales[gi] = f32_to_bf16(scale);
-  biases[gi] = f32_to_bf16(bias);
-
-  // The group's codes fill g*bits/32 whole words of the row's bit stream.
-  uint32_t *dst = w_q + n * (K * bits / 32) + j * (static_cast<int64_t>(g) * bits / 32);
-  uint64_t acc = 0;
-  int nacc = 0;
-  int wi = 0;
-  for (int i = 0; i < g; ++i) {
-    float r = roundf((src[i] - bias) / scale);
-    r = r > n_bins ? n_bins : r;
-    const uint32_t q = static_cast<uint32_t>(static_cast<int>(r));
-    acc |= static_cast<uint64_t>(q) << nacc;
-    nacc += bits;
-    if (nacc >= 32) {
-      dst[wi++] = static_cast<uint32_t>(acc);
-      acc >>= 32;
-      nacc -= 32;
-    }
+  if (live && u == 0) {
+    scales[gi] = f32_to_bf16(scale);
+    biases[gi] = f32_to_bf16(bias);
   }
+
+  uint32_t field = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float r = roundf((v[e] - bias) / scale);
+    r = r > n_bins ? n_bins : r;
+    field |= static_cast<uint32_t>(static_cast<int>(r)) << (bits * e);
+  }
+  __syncthreads();   // words cleared
+  if (live) {
+    const int bit = 4 * bits * u;                    // the field's offset in the group's stream
+    const int wj = gl * wpg + (bit >> 5), sh = bit & 31;
+    atomicOr(&words[wj], field << sh);
+    if (sh + 4 * bits > 32) atomicOr(&words[wj + 1], field >> (32 - sh));
+  }
+  __syncthreads();
+  const int64_t nwords = min(static_cast<int64_t>(S::GPB), ngroups - g0) * wpg;
+  uint32_t *dst = w_q + g0 * wpg;
+  for (int i = threadIdx.x; i < nwords; i += kPackThreads) dst[i] = words[i];
 }
 
 // ----------------------------------------------------------------------------

@@ -565,12 +565,27 @@ int qmv_pack(const float *w, int64_t N, int64_t K, int group_size, int bits, uin
              uint16_t *scales, uint16_t *biases, void *stream) {
   if (int rc = check_common("qmv_pack", N, K, group_size, bits)) return rc;
   if (!w || !w_q || !scales || !biases) return fail(QMV_EINVAL, "qmv_pack: null pointer argument");
+  if (int rc = check_aligned("qmv_pack", w, "w")) return rc;
   const int64_t groups = N * (K / group_size);
-  const int64_t blocks = (groups + 255) / 256;
-  if (blocks > 0x7FFFFFFF) return fail(QMV_EUNSUPPORTED, "qmv_pack: too large");
-  hipLaunchKernelGGL(qmvk::pack_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), w, N, K, group_size, bits, w_q, scales,
-                     biases);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const dim3 block(qmvk::kPackThreads);
+  auto grid = [&](int g) {
+    const int64_t gpb = qmvk::kPackThreads / (g / 4);
+    return (groups + gpb - 1) / gpb;
+  };
+  if (grid(group_size) > 0x7FFFFFFF) return fail(QMV_EUNSUPPORTED, "qmv_pack: too large");
+  const dim3 blocks(static_cast<unsigned>(grid(group_size)));
+  switch (group_size) {
+    case 32:
+      hipLaunchKernelGGL(qmvk::pack_kernel<32>, blocks, block, 0, st, w, groups, bits, w_q, scales, biases);
+      break;
+    case 64:
+      hipLaunchKernelGGL(qmvk::pack_kernel<64>, blocks, block, 0, st, w, groups, bits, w_q, scales, biases);
+      break;
+    default:
+      hipLaunchKernelGGL(qmvk::pack_kernel<128>, blocks, block, 0, st, w, groups, bits, w_q, scales, biases);
+      break;
+  }
   return check_launch("qmv_pack");
 }
 

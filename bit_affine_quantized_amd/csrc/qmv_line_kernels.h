@@ -17,8 +17,8 @@
 // step's loads as well.)  Row blocks follow the XCD order of xcd_block.
 //
 // Measured on MI355X for 14336x4096 4-bit g64 (graph replays over 16
-// rotated input sets, medians of interleaved rounds): loop kernel 8.01 us,
-// straight line 7.87 us, straight line with XCD row order 7.52 us.
+// rotated input sets, medians of interleaved rounds on one box): loop kernel
+// 7.94 us, straight line with XCD row order 7.62-7.80 us.
 #pragma once
 
 #include "qmv_kernels.h"
@@ -165,8 +165,10 @@ __global__ __launch_bounds__(WPB * kWave) void qmv_line_kernel(QmvArgs a) {
 #pragma unroll
   for (int i = 0; i < V; ++i) vals[i] = 0.0f;
 #pragma unroll
-  for (int r = 0; r < RPW; ++r)
-    vals[r] = PAIR ? fmaf(acc[r], 1.0f / static_cast<float>(1 << PairPlan<BITS>::P), accz[r]) : acc[r];
+  for (int r = 0; r < RPW; ++r) {
+    if constexpr (PAIR) vals[r] = fmaf(acc[r], 1.0f / static_cast<float>(1 << PairPlan<BITS>::P), accz[r]);
+    else vals[r] = acc[r];
+  }
   const float tot = wave_reduce_many<V>(vals, lane);
   if (reduce_leader<V>(lane)) {
     const int r = reduce_index<V>(lane);

@@ -72,7 +72,8 @@ enum { QMV_OUT_BF16 = 0, QMV_OUT_F32 = 1 };
  *   if q0 != 0 then s = edge/q0, z = edge, else z = 0;
  *   q = min(round((w - z)/s), 2^bits - 1);  s and z are stored as bf16
  *   (nearest even), the codes use the fp32 values.
- * w: fp32 [N, K].  Outputs: w_q [N, K*bits/32], scales/biases [N, K/group_size].
+ * w: fp32 [N, K], 16-byte aligned.  Outputs: w_q [N, K*bits/32],
+ * scales/biases [N, K/group_size].
  */
 int qmv_pack(const float *w, int64_t N, int64_t K, int group_size, int bits,
              uint32_t *w_q, uint16_t *scales, uint16_t *biases, void *stream);
