@@ -44,15 +44,36 @@ if ROOT not in sys.path:
 METRIC = "qmv GB/s & % of HBM peak, 4-bit g64 N=14336 K=4096 batch 1"
 HBM_PEAK_GBS = 8000.0
 PROFILE_DIR = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = [os.path.join(ROOT, "bit_affine_quantized_amd", "csrc", f)
-                  for f in ("qmv_device.h", "qmv_kernels.h", "qmv_line_kernels.h", "qmv_api.hip",
-                            "pack_kernels.h", "qvm_kernels.h", "qmm_kernels.h")]
+CSRC = os.path.join(ROOT, "bit_affine_quantized_amd", "csrc")
+# the sources whose code a workload's kernels run: the launch logic and the
+# device helpers always, then its kernel family's headers
+COMMON_SOURCES = ("qmv_api.hip", "qmv_device.h")
+FAMILY_SOURCES = {
+    "qmv": ("qmv_kernels.h", "qmv_line_kernels.h"),
+    "qmm": ("qmm_kernels.h", "qvm_kernels.h"),      # matrix cores + slice reduction
+    "ffn": ("qmv_kernels.h",),
+    "moe": ("qmv_kernels.h", "qmm_kernels.h"),
+    "qvm": ("qvm_kernels.h",),
+    "pack": ("pack_kernels.h",),
+}
 ROTATE_BYTES = 512e6
 
 
-def kernel_source_hash() -> str:
+def kernel_sources(workload: str = ""):
+    rows_of_x = int(workload.rsplit("_m", 1)[1]) if re.search(r"_m\d+$", workload) else 1
+    fam = ("pack" if workload.startswith(("pack_", "dequant_")) else
+           "qvm" if workload.startswith("qvm_") else
+           "qmm" if rows_of_x >= 5 else
+           "ffn" if workload.startswith("ffn_") else
+           "moe" if workload.startswith("moe_") else "qmv")
+    return [os.path.join(CSRC, f) for f in COMMON_SOURCES + FAMILY_SOURCES[fam]]
+
+
+def kernel_source_hash(workload: str = "") -> str:
+    """Hash of the sources the workload's kernels are built from: a traffic
+    summary taken on other sources is not used."""
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in kernel_sources(workload):
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -66,7 +87,7 @@ def qbytes(N, K, bits, g):
 def read_traffic(workload: str, src_hash: str):
     """HBM bytes per launch from the committed counter summary for this
     workload, or None if absent or taken on different kernel sources."""
-    path = os.path.join(PROFILE_DIR, f"traffic_{workload}.md")
+    path = os.path.join(PROFILE_DIR, f"{workload}.md")
     try:
         text = open(path).read()
     except OSError:
@@ -380,7 +401,9 @@ def workloads():
     W[h["name"]] = make_qmv(h["N"], h["K"], h["bits"], h["group"], 1, h["name"])
     t = synth.TINY
     W[t["name"]] = make_qmv(t["N"], t["K"], t["bits"], t["group"], 1, t["name"])
-    for M in (1, 4):
+    # 5 rows of x: the first size on the matrix cores (QMV_QMM_MIN_M=6 in
+    # the environment times the same shape on 4-row slabs)
+    for M in (1, 4, 5):
         n = f"decode_qmv_4096x4096_b4_g64_m{M}"
         W[n] = make_qmv(4096, 4096, 4, 64, M, n)
     for bits in (2, 3, 5, 6, 8):
@@ -407,8 +430,10 @@ def workloads():
         n = f"moe_gather_64x2048x2048_b4_g64_t16_top8_{'sorted' if srt else 'unsorted'}"
         W[n] = make_moe(m["E"], m["N"], m["K"], m["bits"], m["group"],
                         m["tokens"], m["top_k"], srt, n)
-    # larger routings (8 and 64 vectors per expert): the matrix-core gather
-    for T in (64, 512):
+    # larger routings: 4 and 5 vectors per expert on either side of the
+    # matrix-core threshold (QMV_GATHER_QMM_MIN in the environment moves it),
+    # and 8 and 64 per expert on the matrix cores
+    for T in (32, 40, 64, 512):
         n = f"moe_gather_64x2048x2048_b4_g64_t{T}_top8_unsorted"
         W[n] = make_moe(m["E"], m["N"], m["K"], m["bits"], m["group"], T, m["top_k"], False, n)
     return W
@@ -622,7 +647,7 @@ def run_workload(wl: Workload, steps: int, warmup: int, want_cpu: bool,
     res["roofline"] = {"bound": "hbm", "achieved": round(gbs, 2),
                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
                        "frac": round(gbs / HBM_PEAK_GBS, 4),
-                       "traffic": read_traffic(wl.name, kernel_source_hash())}
+                       "traffic": read_traffic(wl.name, kernel_source_hash(wl.name))}
     res["cpu_baseline"] = cpu_baseline(wl) if (want_cpu and wl.oracle_fn) \
         else None
     del step

@@ -5,6 +5,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <mutex>
 #include <string>
 
@@ -259,6 +260,22 @@ int launch_gather_t(const qmvk::GatherArgs &a0, int64_t E, hipStream_t st) {
 #define QMV_GATHER_QMM_MIN 5
 #endif
 
+// A path threshold, overridable by a positive integer in the environment
+// variable `name` (read once per process).  The overrides exist to time both
+// paths on one shape; the built-in values are the measured crossovers.
+static int threshold_from_env(const char *name, int builtin) {
+  const char *v = std::getenv(name);
+  if (!v || !*v) return builtin;
+  char *end = nullptr;
+  const long n = std::strtol(v, &end, 10);
+  return (end && *end == '\0' && n > 0 && n < (1L << 30)) ? static_cast<int>(n) : builtin;
+}
+
+static int gather_qmm_min() {
+  static const int v = threshold_from_env("QMV_GATHER_QMM_MIN", QMV_GATHER_QMM_MIN);
+  return v;
+}
+
 template <int BITS, int CPG, int BM>
 int launch_gather_qmm_t(const qmvk::GatherQmmArgs &a0, int64_t E, hipStream_t st) {
   qmvk::GatherQmmArgs a = a0;
@@ -454,6 +471,11 @@ int run_qvm(const uint16_t *x, const uint32_t *w_q, const uint16_t *scales, cons
 // 9.9; 14336x4096 at M = 8: 25.1 vs 19.3)
 #define QMV_QMM_MIN_M 5
 #endif
+
+static int qmm_min_m() {
+  static const int v = threshold_from_env("QMV_QMM_MIN_M", QMV_QMM_MIN_M);
+  return v;
+}
 #ifndef QMV_QMM_WGS
 #define QMV_QMM_WGS 512           // split-K target: workgroups per launch
 #endif
@@ -661,7 +683,7 @@ int qmv_impl(const uint16_t *x, const uint32_t *w_q, const uint16_t *scales, con
     if (int rc = check_aligned("qmv", x, "x")) return rc;
     if (int rc = check_aligned("qmv", w_q, "w_q")) return rc;
   }
-  if (M >= QMV_QMM_MIN_M && N * K * bits / 8 < (int64_t(1) << 32) &&
+  if (M >= qmm_min_m() && N * K * bits / 8 < (int64_t(1) << 32) &&
       N * (K / group_size) * 2 < (int64_t(1) << 32) && 64 * K * 2 < (int64_t(1) << 32)) {
     // (the matrix-core kernel addresses W, scales and biases and a 64-row
     // slab of x with 32-bit byte offsets)
@@ -909,7 +931,7 @@ int gather_qmv(const uint16_t *x, int64_t Bx, const uint32_t *w_q, const uint16_
   hipStream_t st = static_cast<hipStream_t>(stream);
   // Many tokens per expert: the matrix-core gather (the matrix-core kernel
   // addresses x, and each expert's W, scales and biases, with 32-bit offsets)
-  if (P * M >= QMV_GATHER_QMM_MIN * E && Bx * M * K * 2 < (int64_t(1) << 32) &&
+  if (P * M >= static_cast<int64_t>(gather_qmm_min()) * E && Bx * M * K * 2 < (int64_t(1) << 32) &&
       N * K * bits / 8 < (int64_t(1) << 32)) {
     qmvk::GatherQmmArgs g{};
     g.x = x;

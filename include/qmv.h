@@ -86,6 +86,9 @@ int qmv_pack(const float *w, int64_t N, int64_t K, int group_size, int bits,
  *                  the W stream is read once per slab of up to 4 rows.  With
  *                  5 or more rows the matrix cores are used (64-row slabs of
  *                  x, W read once per slab) and K is split into slices.
+ *                  That threshold (5) can be replaced by a positive integer
+ *                  in the environment variable QMV_QMM_MIN_M, read once per
+ *                  process, to time both paths on one shape.
  *   transpose = 0: W packed [K, N] (groups along N, quantized.h qvm and its
  *                  split-K variant); y[m, n] = sum_k x[m, k] * w_hat[k, n].
  *                  N must be a multiple of group_size; W is read once per
@@ -188,7 +191,9 @@ int qmv_silu_gate_resid(const uint16_t *gate, const uint16_t *up,
  * non-decreasing; it may make the call faster and never changes the results
  * (every output is computed with the same arithmetic either way).
  * transpose must be 1 (else QMV_EUNSUPPORTED).  When the routed x vectors
- * average 5 or more per expert (P*M >= 5*E) the matrix cores are used.
+ * average 5 or more per expert (P*M >= 5*E) the matrix cores are used; the
+ * environment variable QMV_GATHER_QMM_MIN (a positive integer, read once per
+ * process) replaces that 5.
  * One expert's packed weight (N*K*bits/8 bytes) must be under 2 GiB (else
  * QMV_EUNSUPPORTED): it is addressed with 32-bit offsets.
  */
