@@ -228,7 +228,7 @@ __global__ __launch_bounds__(256) void unpack_kernel(const uint32_t *__restrict_
     static_for<0, 16>([&](auto i) {
       constexpr int I = decltype(i)::value;
       uint32_t lo, hi;
-      pair_codes<BITS>(make_pair<BITS, I>(w, pk), lo, hi);
+      pair_codes<BITS, I>(make_pair<BITS, I>(w, pk), lo, hi);
       out[PairPlan<BITS>::lo(I)] = static_cast<uint8_t>(lo);
       out[PairPlan<BITS>::hi(I)] = static_cast<uint8_t>(hi);
     });

@@ -156,7 +156,7 @@ template <int BITS, int MV, int XIN>
 int launch_qmv_t(const qmvk::QmvArgs &a, hipStream_t st) {
   constexpr bool PAIR = (BITS <= 6) && (XIN == qmvk::XIN_PLAIN);
   const int64_t Kc = a.K / 32;
-  const int64_t lds = Kc * qmvk::chunk_stride<PAIR, (XIN == qmvk::XIN_SILU ? 1 : MV)>();
+  const int64_t lds = Kc * qmvk::chunk_stride_for<BITS, PAIR, (XIN == qmvk::XIN_SILU ? 1 : MV)>();
   if constexpr (XIN == qmvk::XIN_PLAIN && MV == 1) {
     if (Kc <= 2 * qmvk::kWave && !QMV_FORCE_WPB) {
       if (static_cast<int64_t>(a.nmat) * a.N <= QMV_SMALL_ROWS) return launch_line_cpl<BITS, 1, 8>(a, lds, st);
@@ -186,7 +186,8 @@ int launch_qmv_bits(int bits, const qmvk::QmvArgs &a, hipStream_t st) {
 
 int64_t qmv_lds_bytes(int bits, int mv, int64_t K) {
   const bool pair = bits <= 6;
-  return (K / 32) * (mv * (pair ? 64 : 128) + 16);
+  const bool two = bits == 3 || bits == 5;   // second chunk sum (PairPlan)
+  return (K / 32) * (mv * (pair ? 64 : 128) + (two ? 48 : 16));
 }
 
 // ------------------------------------------------------------------ gather
@@ -221,7 +222,7 @@ int launch_gather_t(const qmvk::GatherArgs &a0, int64_t E, hipStream_t st) {
   constexpr int kGatherMv = gather_mv<BITS>();
   qmvk::GatherArgs a = a0;
   const int64_t Kc = a.K / 32;
-  const int64_t lds_x = Kc * qmvk::chunk_stride<(BITS <= 6), kGatherMv>();
+  const int64_t lds_x = Kc * qmvk::chunk_stride_for<BITS, (BITS <= 6), kGatherMv>();
   // Tiles of `tile_rows` rows: many small workgroups (~8 per CU over the
   // expert stack), so that most of the weight stream is in flight at once,
   // yet enough rows per tile that routing and x staging are paid once per

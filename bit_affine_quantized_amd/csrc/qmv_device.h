@@ -88,7 +88,9 @@ struct PairConsts {
 
 template <int BITS>
 __device__ __forceinline__ PairConsts pair_consts() {
-  const uint32_t m = BITS == 4 ? 0x00780078u : BITS == 2 ? 0x00600060u : 0u;
+  // the code bits of both halves of a pair built by shift/window + and-or
+  const uint32_t m = BITS == 4 ? 0x00780078u : BITS == 2 ? 0x00600060u
+                   : BITS == 3 ? 0x00380070u : BITS == 5 ? 0x003E007Cu : 0u;
   return PairConsts{opaque_sgpr(m), opaque_vgpr(kMagic2)};
 }
 
@@ -115,23 +117,48 @@ __device__ __forceinline__ uint32_t code_at(const uint32_t (&w)[BITS]) {
 
 // ----------------------------------------------------------------------------
 // Pair plans: which two codes of a chunk share bf16 pair i (i = 0..15).  The
-// x staging uses the same plan, so any pairing is valid; the plans below are
-// chosen so that for b = 2 and 4 one shift and one and-or build each pair
-// (the two codes sit exactly 16 bits apart in one word).
+// x staging uses the same plan, so any pairing is valid.  The plans are
+// chosen so that one shift (or one alignbit window) and one and-or build a
+// pair:
+//  * b = 2, 4: the two codes sit exactly 16 bits apart in one word.
+//  * b = 3, 5: no two codes are 16 bits apart, but codes k and k + 5 (3-bit)
+//    or k + 3 (5-bit) are 15 bits apart.  One 32-bit window of the stream
+//    puts code k at mantissa bit P and its partner one bit lower in the high
+//    half, at P - 1: that half holds 128 + q * 2^(P-1).  Its x is staged
+//    doubled (exact in bf16), so the product is (256 + q * 2^P) * x: the same
+//    q * 2^P * x as the low half, and 256 x in place of 128 x.  Each chunk
+//    then carries two sums, X = sum x and X' = sum of the staged x values (x
+//    of the low halves plus 2x of the doubled high halves), and the fold is
+//        2^-P * s*D + z*X - 2^b * s*X'.
+//    15 pairs are built this way; codes 30 and 31 form a plain pair (both
+//    halves at P, x not doubled).
+//  * b = 6: codes i and i + 16, each extracted on its own.
 // ----------------------------------------------------------------------------
 template <int BITS>
 struct PairPlan {
-  static constexpr int P = 7 - BITS;   // mantissa position of the code
+  static constexpr int P = 7 - BITS;   // mantissa position of the (low) code
+  static constexpr bool kWindow = BITS == 3 || BITS == 5;   // 15-bit-apart pairs
+  static constexpr int kGap = BITS == 3 ? 5 : 3;             // partner distance (codes)
+  static constexpr int kBlock = 2 * kGap;                   // codes per block of pairs
   // code index of the low / high half of pair i
   static constexpr __host__ __device__ int lo(int i) {
     return BITS == 4 ? 8 * (i >> 2) + (i & 3)
          : BITS == 2 ? 16 * (i >> 3) + (i & 7)
+         : kWindow ? (i < 15 ? kBlock * (i / kGap) + i % kGap : 30)
          : i;
   }
   static constexpr __host__ __device__ int hi(int i) {
-    return BITS == 4 ? lo(i) + 4 : BITS == 2 ? lo(i) + 8 : i + 16;
+    return BITS == 4 ? lo(i) + 4 : BITS == 2 ? lo(i) + 8
+         : kWindow ? (i < 15 ? lo(i) + kGap : 31)
+         : i + 16;
   }
+  // the high half of pair i holds its code at P - 1 and meets doubled x
+  static constexpr __host__ __device__ bool doubled(int i) { return kWindow && i < 15; }
 };
+
+// whether a chunk's staging carries the second sum X' (see PairPlan)
+template <int BITS>
+constexpr bool two_sums() { return PairPlan<BITS>::kWindow; }
 
 template <int BITS, int I>
 __device__ __forceinline__ uint32_t make_pair(const uint32_t (&w)[BITS], PairConsts k) {
@@ -144,18 +171,32 @@ __device__ __forceinline__ uint32_t make_pair(const uint32_t (&w)[BITS], PairCon
     constexpr int d = I >> 3, j = I & 7;
     // code j at bit 2j -> bit 5; code j+8 at bit 2j+16 -> bit 21
     return (shl_signed<5 - 2 * j>(w[d]) & k.mask) | k.magic;
+  } else if constexpr (PairPlan<BITS>::doubled(I)) {
+    // the 22-bit window whose bit P is code lo's first bit: code hi then
+    // sits at bit 16 + P - 1
+    constexpr int s = BITS * PairPlan<BITS>::lo(I) - P;   // stream bit at window bit 0
+    uint32_t win;
+    if constexpr (s < 0) {
+      win = w[0] << (-s);
+    } else {
+      constexpr int j = s >> 5, o = s & 31;
+      if constexpr (o + 22 <= 32) win = w[j] >> o;
+      else win = __builtin_amdgcn_alignbit(w[j + 1], w[j], o);
+    }
+    return (win & k.mask) | k.magic;
   } else {
     constexpr int klo = PairPlan<BITS>::lo(I), khi = PairPlan<BITS>::hi(I);
     return (code_at<BITS, klo>(w) << P) | (code_at<BITS, khi>(w) << (16 + P)) | k.magic;
   }
 }
 
-// Recover code index / value of both halves from a built pair (debug export).
-template <int BITS>
+// Recover the codes of both halves of built pair I (debug export).
+template <int BITS, int I>
 __device__ __forceinline__ void pair_codes(uint32_t p, uint32_t &lo, uint32_t &hi) {
   constexpr int P = PairPlan<BITS>::P;
+  constexpr int PH = PairPlan<BITS>::doubled(I) ? P - 1 : P;
   lo = (p & 0x7Fu) >> P;
-  hi = ((p >> 16) & 0x7Fu) >> P;
+  hi = ((p >> 16) & 0x7Fu) >> PH;
 }
 
 // Code k of a chunk as fp32 (fp32 path).  Bytes use v_cvt_f32_ubyteN.

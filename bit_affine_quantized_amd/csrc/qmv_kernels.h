@@ -27,18 +27,23 @@ struct MatDesc {
 };
 
 // Staged-x layout in LDS, chunk-major: chunk c of the staged vectors starts
-// at c * chunk_stride<PAIR, MV>(); vector m's data sits at m * vec_bytes and
-// the MV fp32 chunk sums follow, in a 16-byte tail.  Every offset inside a
-// chunk is a compile-time immediate, and the strides (80/144/272 bytes for
-// bf16 pairs, 144/272/528 for fp32) put 16 consecutive lanes on 16 distinct
-// 4-bank quads of LDS, so 128-bit reads do not conflict.
+// at c * chunk_stride<PAIR, MV, TWO>(); vector m's data sits at m * vec_bytes
+// and the MV fp32 chunk sums X follow, in a 16-byte tail; with TWO (3- and
+// 5-bit pairs, see PairPlan) the tail is 48 bytes and the MV second sums X'
+// follow the first.  Every offset inside a chunk is a compile-time
+// immediate, and the strides (an odd multiple of 16 bytes: 80/144/272 or
+// 112/176/304 for bf16 pairs, 144/272/528 for fp32) put 16 consecutive lanes
+// on 16 distinct 4-bank quads of LDS, so 128-bit reads do not conflict.
 template <bool PAIR>
 constexpr int vec_bytes() { return PAIR ? 64 : 128; }
-template <bool PAIR, int MV>
+template <bool PAIR, int MV, bool TWO = false>
 constexpr int chunk_stride() {
   static_assert(MV >= 1 && MV <= 4, "at most 4 staged x vectors");
-  return MV * vec_bytes<PAIR>() + 16;
+  return MV * vec_bytes<PAIR>() + (TWO ? 48 : 16);
 }
+// the staged layout of a kernel for BITS-bit codes
+template <int BITS, bool PAIR, int MV>
+constexpr int chunk_stride_for() { return chunk_stride<PAIR, MV, PAIR && two_sums<BITS>()>(); }
 template <bool PAIR>
 constexpr int stage_bytes_per_chunk() { return vec_bytes<PAIR>() + 16; }   // one vector (host sizing)
 
@@ -67,10 +72,11 @@ __device__ __forceinline__ float raw_x(const uint32_t (&raw)[16], int k) {
 template <int BITS, int MV>
 __device__ __forceinline__ void stage_pairs_raw(const uint32_t (&raw)[16], unsigned char *lds,
                                                 int m, int c) {
-  float sum = 0.0f;
+  constexpr bool TWO = two_sums<BITS>();
+  float sum = 0.0f, sum2 = 0.0f;
 #pragma unroll
   for (int k = 0; k < 16; ++k) sum = dot2_bf16(raw[k], 0x3F803F80u, sum);
-  unsigned char *chunk = lds + c * chunk_stride<true, MV>();
+  unsigned char *chunk = lds + c * chunk_stride<true, MV, TWO>();
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     uint32_t pr[4];
@@ -81,10 +87,17 @@ __device__ __forceinline__ void stage_pairs_raw(const uint32_t (&raw)[16], unsig
       // v_perm_b32(S0, S1, sel): selector bytes 0-3 pick S1's bytes, 4-7 S0's
       const uint32_t sel = ((khi & 1) ? 0x07060000u : 0x05040000u) | ((klo & 1) ? 0x0302u : 0x0100u);
       pr[e] = __builtin_amdgcn_perm(raw[khi >> 1], raw[klo >> 1], sel);
+      if (PairPlan<BITS>::doubled(i)) {
+        // high half x -> 2x: an exact fp32 product whose low 16 bits stay 0
+        const float h2 = 2.0f * __uint_as_float(pr[e] & 0xFFFF0000u);
+        pr[e] = (pr[e] & 0xFFFFu) | __float_as_uint(h2);
+      }
+      if constexpr (TWO) sum2 = dot2_bf16(pr[e], 0x3F803F80u, sum2);
     }
     *reinterpret_cast<uint4 *>(chunk + m * 64 + q * 16) = make_uint4(pr[0], pr[1], pr[2], pr[3]);
   }
   reinterpret_cast<float *>(chunk + MV * 64)[m] = sum;
+  if constexpr (TWO) reinterpret_cast<float *>(chunk + MV * 64)[MV + m] = sum2;
 }
 
 template <int BITS, int MV>
@@ -166,6 +179,7 @@ __device__ __forceinline__ void accumulate_chunk(const ChunkStep<BITS, RPW> &st,
                                                  int nv, PairConsts pk,
                                                  float (&acc)[RPW][MV], float (&accz)[RPW][MV]) {
   const float *sums = reinterpret_cast<const float *>(chunk + MV * vec_bytes<PAIR>());
+  constexpr bool TWO = PAIR && two_sums<BITS>();   // sums[MV + m] holds X' (PairPlan)
   if constexpr (PAIR && MV == 1) {
     // one x vector: keep its pairs in registers, build one row's pairs at a time
     uint32_t xp[16];
@@ -175,10 +189,12 @@ __device__ __forceinline__ void accumulate_chunk(const ChunkStep<BITS, RPW> &st,
       xp[4 * q] = v.x; xp[4 * q + 1] = v.y; xp[4 * q + 2] = v.z; xp[4 * q + 3] = v.w;
     }
     const float xs = sums[0];
+    const float xs2 = TWO ? sums[1] : 0.0f;
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
       const float s = st.scale(r);
-      const float zc = fmaf(-static_cast<float>(1 << BITS), s, st.bias(r));  // z - 2^b s
+      // coefficient of X: z - 2^b s, or z with the second sum X' (times -2^b s)
+      const float zc = TWO ? st.bias(r) : fmaf(-static_cast<float>(1 << BITS), s, st.bias(r));
       float d = 0.0f;
       static_for<0, 16>([&](auto i) {
         constexpr int I = decltype(i)::value;
@@ -186,6 +202,7 @@ __device__ __forceinline__ void accumulate_chunk(const ChunkStep<BITS, RPW> &st,
       });
       acc[r][0] = fmaf(s, d, acc[r][0]);
       accz[r][0] = fmaf(zc, xs, accz[r][0]);
+      if constexpr (TWO) accz[r][0] = fmaf(-static_cast<float>(1 << BITS) * s, xs2, accz[r][0]);
     }
   } else if constexpr (PAIR) {
     // build every row's pairs once, then stream the x vectors past them
@@ -194,7 +211,8 @@ __device__ __forceinline__ void accumulate_chunk(const ChunkStep<BITS, RPW> &st,
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
       sc[r] = st.scale(r);
-      zc[r] = fmaf(-static_cast<float>(1 << BITS), sc[r], st.bias(r));  // z - 2^b s
+      // coefficient of X: z - 2^b s, or z with the second sum X' (times -2^b s)
+      zc[r] = TWO ? st.bias(r) : fmaf(-static_cast<float>(1 << BITS), sc[r], st.bias(r));
       static_for<0, 16>([&](auto i) { pr[r][decltype(i)::value] = make_pair<BITS, decltype(i)::value>(st.w[r], pk); });
     }
 #pragma unroll
@@ -207,6 +225,7 @@ __device__ __forceinline__ void accumulate_chunk(const ChunkStep<BITS, RPW> &st,
           xp[4 * q] = v.x; xp[4 * q + 1] = v.y; xp[4 * q + 2] = v.z; xp[4 * q + 3] = v.w;
         }
         const float xs = sums[m];
+        const float xs2 = TWO ? sums[MV + m] : 0.0f;
 #pragma unroll
         for (int r = 0; r < RPW; ++r) {
           float d = 0.0f;
@@ -214,6 +233,7 @@ __device__ __forceinline__ void accumulate_chunk(const ChunkStep<BITS, RPW> &st,
           for (int i = 0; i < 16; ++i) d = dot2_bf16(pr[r][i], xp[i], d);
           acc[r][m] = fmaf(sc[r], d, acc[r][m]);
           accz[r][m] = fmaf(zc[r], xs, accz[r][m]);
+          if constexpr (TWO) accz[r][m] = fmaf(-static_cast<float>(1 << BITS) * sc[r], xs2, accz[r][m]);
         }
       }
       // keep one vector's x pairs live at a time (no hoisting of the next
@@ -328,7 +348,7 @@ struct WaveEngine {
                                           const unsigned char *lds, int nv) {
     const int c = step * kWave + lane;
     if (c >= Kc) return;
-    accumulate_chunk<BITS, RPW, MV, PAIR>(st, lds + c * chunk_stride<PAIR, MV>(), nv, pk, acc, accz);
+    accumulate_chunk<BITS, RPW, MV, PAIR>(st, lds + c * chunk_stride_for<BITS, PAIR, MV>(), nv, pk, acc, accz);
   }
 
   // Issue the first two steps' loads (before x staging); with one step the
@@ -516,13 +536,16 @@ __device__ __forceinline__ void gather_chunk_pairs(const uint32_t (&w)[BITS], ui
     }
     __builtin_amdgcn_sched_barrier(0);   // keep the next quad's reads below this one
   });
+  constexpr bool TWO = two_sums<BITS>();   // sums[MV + m] holds X' (PairPlan)
   const float *sums = reinterpret_cast<const float *>(chunk + MV * 64);
   const float s = bf16_to_f32(sb);
-  const float zc = fmaf(-static_cast<float>(1 << BITS), s, bf16_to_f32(bb));   // z - 2^b s
+  // coefficient of X: z - 2^b s, or z with the second sum X' (times -2^b s)
+  const float zc = TWO ? bf16_to_f32(bb) : fmaf(-static_cast<float>(1 << BITS), s, bf16_to_f32(bb));
 #pragma unroll
   for (int m = 0; m < NV; ++m) {
     acc[0][m] = fmaf(s, d[m], acc[0][m]);
     accz[0][m] = fmaf(zc, sums[m], accz[0][m]);
+    if constexpr (TWO) accz[0][m] = fmaf(-static_cast<float>(1 << BITS) * s, sums[MV + m], accz[0][m]);
   }
 }
 
@@ -740,7 +763,7 @@ __global__ __launch_bounds__(GW * kWave) void gather_kernel(GatherArgs a) {
         for (int m = 0; m < MV; ++m) acc[0][m] = accz[0][m] = 0.0f;
 
         int c_rg = 0, c_ks = 0;
-        constexpr int kStride = chunk_stride<PAIR, MV>();
+        constexpr int kStride = chunk_stride_for<BITS, PAIR, MV>();
         const unsigned char *xlane = smem + u * kStride;    // this lane's first staged chunk
         auto consume = [&](const ChunkStep<BITS, CPL> &st) {
           const int left = Kc - c_ks * KS;                 // chunks of this K range that exist

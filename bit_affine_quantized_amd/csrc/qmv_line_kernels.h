@@ -32,7 +32,8 @@ template <int BITS, int RPW, int WPB, int CPL, bool FULL>
 __global__ __launch_bounds__(WPB * kWave) void qmv_line_kernel(QmvArgs a) {
   constexpr int NT = WPB * kWave;
   constexpr bool PAIR = BITS <= 6;
-  constexpr int kStride = chunk_stride<PAIR, 1>();
+  constexpr int kStride = chunk_stride_for<BITS, PAIR, 1>();
+  constexpr bool TWO = PAIR && two_sums<BITS>();   // X' follows X (PairPlan)
   constexpr int XI = (CPL * kWave + NT - 1) / NT;   // x staging items per thread
   extern __shared__ __align__(16) unsigned char smem[];
 
@@ -116,6 +117,7 @@ __global__ __launch_bounds__(WPB * kWave) void qmv_line_kernel(QmvArgs a) {
     const bool live = FULL || (t + 1) * kWave <= Kc || t * kWave + lane < Kc;
     const unsigned char *chunk = smem + chunk_of(t) * kStride;
     const float xs = *reinterpret_cast<const float *>(chunk + vec_bytes<PAIR>());
+    const float xs2 = TWO ? *reinterpret_cast<const float *>(chunk + vec_bytes<PAIR>() + 4) : 0.0f;
     if constexpr (PAIR) {
       uint32_t xp[16];
 #pragma unroll
@@ -131,10 +133,12 @@ __global__ __launch_bounds__(WPB * kWave) void qmv_line_kernel(QmvArgs a) {
           d = dot2_bf16(make_pair<BITS, I>(w[t][r], pk), xp[I], d);
         });
         float s = bf16_to_f32(sv[t][r]);
-        float zc = fmaf(-static_cast<float>(1 << BITS), s, bf16_to_f32(bv[t][r]));   // z - 2^b s
+        // coefficient of X: z - 2^b s, or z with the second sum X' (times -2^b s)
+        float zc = TWO ? bf16_to_f32(bv[t][r]) : fmaf(-static_cast<float>(1 << BITS), s, bf16_to_f32(bv[t][r]));
         if (!live) s = zc = 0.0f;
         acc[r] = fmaf(s, d, acc[r]);
         accz[r] = fmaf(zc, xs, accz[r]);
+        if constexpr (TWO) accz[r] = fmaf(-static_cast<float>(1 << BITS) * s, xs2, accz[r]);
       }
     } else {
       float xf[32];
