@@ -90,7 +90,8 @@ template <int BITS>
 __device__ __forceinline__ PairConsts pair_consts() {
   // the code bits of both halves of a pair built by shift/window + and-or
   const uint32_t m = BITS == 4 ? 0x00780078u : BITS == 2 ? 0x00600060u
-                   : BITS == 3 ? 0x00380070u : BITS == 5 ? 0x003E007Cu : 0u;
+                   : BITS == 3 ? 0x00380070u : BITS == 5 ? 0x003E007Cu
+                   : BITS == 6 ? 0x007E007Eu : 0u;
   return PairConsts{opaque_sgpr(m), opaque_vgpr(kMagic2)};
 }
 
@@ -132,8 +133,54 @@ __device__ __forceinline__ uint32_t code_at(const uint32_t (&w)[BITS]) {
 //        2^-P * s*D + z*X - 2^b * s*X'.
 //    15 pairs are built this way; codes 30 and 31 form a plain pair (both
 //    halves at P, x not doubled).
-//  * b = 6: codes i and i + 16, each extracted on its own.
+//  * b = 6: code k = 4m + r lies in byte group m (bytes 3m..3m+2) at bits
+//    6r..6r+5 of the group, in one byte (r = 0, 3) or two (r = 1, 2).  A pair
+//    joins the same r of two groups: one v_perm_b32 gathers the code's
+//    byte(s) of each group into its half, one shift moves both codes to
+//    mantissa bit 1 (P = 1), and one and-or finishes.  The group pairs of
+//    each r are chosen so that the four bytes lie in at most two words.
 // ----------------------------------------------------------------------------
+struct SixBitPlan {
+  // group pairs (m, m') of pair j of class r
+  static constexpr int kGroups[4][4][2] = {{{0, 1}, {2, 3}, {4, 5}, {6, 7}},
+                                           {{1, 0}, {5, 4}, {2, 3}, {6, 7}},
+                                           {{2, 1}, {6, 5}, {0, 3}, {4, 7}},
+                                           {{0, 1}, {2, 3}, {4, 5}, {6, 7}}};
+  static constexpr int kByte0[4] = {0, 0, 1, 2};    // first byte of the code in its group
+  static constexpr int kByte1[4] = {-1, 1, 2, -1};  // second byte, if any
+  static constexpr int kShift[4] = {-1, 5, 3, 1};   // right shift to bit 1 (-1: left by 1)
+  // chunk byte at position pos (0, 1: low half; 2, 3: high half) of pair i, or -1
+  static constexpr int byte_of(int i, int pos) {
+    const int r = i >> 2, j = i & 3;
+    const int m = kGroups[r][j][pos >> 1];
+    const int b = (pos & 1) ? kByte1[r] : kByte0[r];
+    return b < 0 ? -1 : 3 * m + b;
+  }
+  static constexpr int word_a(int i) {   // lower source word
+    int d = 1 << 20;
+    for (int pos = 0; pos < 4; ++pos)
+      if (byte_of(i, pos) >= 0 && (byte_of(i, pos) >> 2) < d) d = byte_of(i, pos) >> 2;
+    return d;
+  }
+  static constexpr int word_b(int i) {   // upper source word
+    int d = -1;
+    for (int pos = 0; pos < 4; ++pos)
+      if (byte_of(i, pos) >= 0 && (byte_of(i, pos) >> 2) > d) d = byte_of(i, pos) >> 2;
+    return d;
+  }
+  // v_perm_b32 selector: 0-3 pick word_a's bytes, 4-7 word_b's, 0x0C a zero
+  static constexpr uint32_t selector(int i) {
+    uint32_t sel = 0;
+    for (int pos = 0; pos < 4; ++pos) {
+      const int b = byte_of(i, pos);
+      const uint32_t v = b < 0 ? 0x0Cu : (b >> 2) == word_a(i) ? static_cast<uint32_t>(b & 3)
+                                                                : 4u + static_cast<uint32_t>(b & 3);
+      sel |= v << (8 * pos);
+    }
+    return sel;
+  }
+};
+
 template <int BITS>
 struct PairPlan {
   static constexpr int P = 7 - BITS;   // mantissa position of the (low) code
@@ -145,11 +192,13 @@ struct PairPlan {
     return BITS == 4 ? 8 * (i >> 2) + (i & 3)
          : BITS == 2 ? 16 * (i >> 3) + (i & 7)
          : kWindow ? (i < 15 ? kBlock * (i / kGap) + i % kGap : 30)
+         : BITS == 6 ? 4 * SixBitPlan::kGroups[i >> 2][i & 3][0] + (i >> 2)
          : i;
   }
   static constexpr __host__ __device__ int hi(int i) {
     return BITS == 4 ? lo(i) + 4 : BITS == 2 ? lo(i) + 8
          : kWindow ? (i < 15 ? lo(i) + kGap : 31)
+         : BITS == 6 ? 4 * SixBitPlan::kGroups[i >> 2][i & 3][1] + (i >> 2)
          : i + 16;
   }
   // the high half of pair i holds its code at P - 1 and meets doubled x
@@ -171,6 +220,11 @@ __device__ __forceinline__ uint32_t make_pair(const uint32_t (&w)[BITS], PairCon
     constexpr int d = I >> 3, j = I & 7;
     // code j at bit 2j -> bit 5; code j+8 at bit 2j+16 -> bit 21
     return (shl_signed<5 - 2 * j>(w[d]) & k.mask) | k.magic;
+  } else if constexpr (BITS == 6) {
+    constexpr uint32_t sel = SixBitPlan::selector(I);
+    constexpr int sh = SixBitPlan::kShift[I >> 2];
+    const uint32_t v = __builtin_amdgcn_perm(w[SixBitPlan::word_b(I)], w[SixBitPlan::word_a(I)], sel);
+    return (shl_signed<-sh>(v) & k.mask) | k.magic;
   } else if constexpr (PairPlan<BITS>::doubled(I)) {
     // the 22-bit window whose bit P is code lo's first bit: code hi then
     // sits at bit 16 + P - 1
