@@ -340,6 +340,56 @@ int launch_unpack_t(const uint32_t *w_q, int64_t N, int64_t K, uint8_t *codes, h
   return check_launch("qmv_unpack_codes");
 }
 
+// ------------------------------------------------------------------ QMV_DEBUG
+// With QMV_DEBUG set in the environment (non-empty, not "0"; read on every
+// call), gather_qmv checks its index preconditions on the device first and
+// waits for the answer.
+bool debug_enabled() {
+  const char *v = std::getenv("QMV_DEBUG");
+  return v && *v && !(v[0] == '0' && v[1] == '\0');
+}
+
+__global__ __launch_bounds__(256) void check_indices_kernel(const uint32_t *__restrict__ lhs,
+                                                            const uint32_t *__restrict__ rhs, int64_t P,
+                                                            int64_t Bx, int64_t E, uint32_t *bad) {
+  const int64_t p = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (p < P && (static_cast<int64_t>(lhs[p]) >= Bx || static_cast<int64_t>(rhs[p]) >= E)) *bad = 1u;
+}
+
+__global__ void clear_flag_kernel(uint32_t *flag) { *flag = 0u; }
+
+// QMV_OK if every lhs[p] < Bx and rhs[p] < E, QMV_EINVAL if not.  Skipped
+// (QMV_OK) while the stream is being captured: the check must wait for the
+// device, which a capture cannot.
+int check_gather_indices(const uint32_t *lhs, const uint32_t *rhs, int64_t P, int64_t Bx, int64_t E,
+                         hipStream_t st) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cs) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(QMV_EHIP, "gather_qmv: QMV_DEBUG: hipStreamIsCapturing failed");
+  }
+  if (cs != hipStreamCaptureStatusNone) return QMV_OK;
+  uint32_t *flag = nullptr;
+  if (hipMallocAsync(reinterpret_cast<void **>(&flag), sizeof(uint32_t), st) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(QMV_EHIP, "gather_qmv: QMV_DEBUG: allocating the check flag failed");
+  }
+  hipLaunchKernelGGL(clear_flag_kernel, dim3(1), dim3(1), 0, st, flag);
+  const int64_t blocks = (P + 255) / 256;
+  hipLaunchKernelGGL(check_indices_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, lhs, rhs,
+                     P, Bx, E, flag);
+  uint32_t bad = 0;
+  const bool ok = hipMemcpyAsync(&bad, flag, sizeof(bad), hipMemcpyDeviceToHost, st) == hipSuccess &&
+                  hipFreeAsync(flag, st) == hipSuccess && hipStreamSynchronize(st) == hipSuccess;
+  if (!ok) {
+    (void)hipGetLastError();
+    return fail(QMV_EHIP, "gather_qmv: QMV_DEBUG: the index check failed to run");
+  }
+  if (bad) return fail(QMV_EINVAL, "gather_qmv: QMV_DEBUG: an index is out of range (need lhs < Bx = %lld "
+                       "and rhs < E = %lld for all %lld pairs)", (long long)Bx, (long long)E, (long long)P);
+  return QMV_OK;
+}
+
 // ------------------------------------------------------------------ workspace
 // The split-K paths (transpose = 0, and 5 or more rows of x on the matrix
 // cores) write the S slices' fp32 partial sums to a workspace that a second
@@ -910,6 +960,10 @@ int gather_qmv(const uint16_t *x, int64_t Bx, const uint32_t *w_q, const uint16_
     return fail(QMV_EUNSUPPORTED, "gather_qmv: K=%lld too large", (long long)K);
   if (M > (int64_t(1) << 20) || P > (int64_t(1) << 30))
     return fail(QMV_EUNSUPPORTED, "gather_qmv: M or P too large");
+  if (debug_enabled()) {
+    if (int rc = check_gather_indices(lhs_indices, rhs_indices, P, Bx, E, static_cast<hipStream_t>(stream)))
+      return rc;
+  }
   // one expert's words, scales and biases are addressed with 32-bit offsets
   if (N * (K / 32) * bits * 4 + 64 * (K / 32) * bits * 4 >= (int64_t(1) << 31))
     return fail(QMV_EUNSUPPORTED, "gather_qmv: one expert's packed weight must be under 2 GiB");

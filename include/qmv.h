@@ -196,6 +196,14 @@ int qmv_silu_gate_resid(const uint16_t *gate, const uint16_t *up,
  * process) replaces that 5.
  * One expert's packed weight (N*K*bits/8 bytes) must be under 2 GiB (else
  * QMV_EUNSUPPORTED): it is addressed with 32-bit offsets.
+ * Indices must satisfy lhs[p] < Bx and rhs[p] < E (the pages leave checking
+ * them to the caller).  Without a check, a pair with rhs[p] >= E is never
+ * routed (its rows of y are not written) and lhs[p] >= Bx reads x row
+ * Bx - 1; nothing is read out of bounds.  With the environment variable
+ * QMV_DEBUG set (non-empty and not "0"; read on every call) the call first
+ * checks every index on the device, waits for the stream, and returns
+ * QMV_EINVAL if one is out of range; the check is skipped while the stream
+ * is being captured into a HIP graph.
  */
 int gather_qmv(const uint16_t *x, int64_t Bx, const uint32_t *w_q,
                const uint16_t *scales, const uint16_t *biases, int64_t E,
