@@ -692,10 +692,12 @@ def copy_reference(nbytes: int, steps: int):
             "frac_of_8TBs": round(2 * n / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
-def read_reference(nbytes: int, rows: int, steps: int):
+def read_reference(nbytes: int, rows: int, steps: int, split=None):
     """The streaming-read reference (libqmv_bench.so, qmv_bench_read) over
     `nbytes` bytes, rotated over >= 512 MB and timed like the workloads:
-    alone, and writing one bf16 per row-sized span as a matvec writes y."""
+    alone, and writing one bf16 per row-sized span as a matvec writes y.
+    With `split` = (weight bytes, bytes of each of scales and biases) also
+    the three-array read a matvec must do (qmv_bench_read3), with y."""
     import ctypes
     import torch
     from bit_affine_quantized_amd import _build
@@ -703,6 +705,9 @@ def read_reference(nbytes: int, rows: int, steps: int):
     L.qmv_bench_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
                                  ctypes.c_uint64, ctypes.c_void_p]
     L.qmv_bench_read.restype = ctypes.c_int
+    L.qmv_bench_read3.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p,
+                                  ctypes.c_uint64, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
+    L.qmv_bench_read3.restype = ctypes.c_int
     n = (nbytes // 16) * 16
     every = max(16, (n // rows) // 16 * 16)
     sets = max(2, math.ceil(ROTATE_BYTES / n))
@@ -732,6 +737,34 @@ def read_reference(nbytes: int, rows: int, steps: int):
                       "queue_drained": info.get("queue_drained")}
         if store:
             out[label]["outputs"] = n // every
+    if split is not None:
+        wb, sbb = split
+        sets3 = max(2, math.ceil(ROTATE_BYTES / (wb + 2 * sbb)))
+        bufs3 = [(torch.randint(0, 255, (wb,), dtype=torch.uint8, device="cuda"),
+                  torch.randint(0, 255, (sbb,), dtype=torch.uint8, device="cuda"),
+                  torch.randint(0, 255, (sbb,), dtype=torch.uint8, device="cuda"),
+                  torch.empty(rows, dtype=torch.int16, device="cuda")) for _ in range(sets3)]
+        torch.cuda.synchronize()
+
+        def step3(i, stream):
+            w, sc, bi, y = bufs3[i % sets3]
+            rc = L.qmv_bench_read3(ctypes.c_void_p(w.data_ptr()), wb, ctypes.c_void_p(sc.data_ptr()),
+                                   ctypes.c_void_p(bi.data_ptr()), sbb, rows,
+                                   ctypes.c_void_p(y.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
+            if rc:
+                raise RuntimeError(f"qmv_bench_read3 failed: {rc}")
+        stream = torch.cuda.current_stream()
+        for i in range(20):
+            step3(i, stream)
+        info = {}
+        ms = _time_queued(step3, steps, stream, info)
+        tot = wb + 2 * sbb
+        out["read3_and_store"] = {"weight_bytes": wb, "scale_bytes": sbb, "bias_bytes": sbb,
+                                  "ms_per_launch": round(ms, 6),
+                                  "GBs": round(tot / (ms * 1e-3) / 1e9, 1),
+                                  "frac_of_8TBs": round(tot / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                  "graph_ms_per_launch": round(_time_graph(step3, steps, 0), 6),
+                                  "queue_drained": info.get("queue_drained"), "outputs": rows}
     return out
 
 
@@ -776,8 +809,13 @@ def main():
     if args.read_reference:
         n = args.workload or synth.HEADLINE["name"]
         rows = synth.HEADLINE["N"] if n == synth.HEADLINE["name"] else 4096
+        split = None
+        mq = re.match(r"(?:decode_)?qmv_(\d+)x(\d+)_b(\d+)_g(\d+)_m1$", n)
+        if mq:                                  # one-vector matvec: W, scales, biases
+            N_, K_, b_, g_ = (int(v) for v in mq.groups())
+            split = (N_ * K_ * b_ // 8, 2 * N_ * (K_ // g_))
         print(json.dumps({"workload": n, **read_reference(W[n].nbytes, rows,
-                                                          args.steps)}))
+                                                          args.steps, split)}))
         return
     names = list(W) if args.all else [args.workload or synth.HEADLINE["name"]]
     for n in names:
