@@ -61,12 +61,15 @@ __global__ __launch_bounds__(WPB * kWave) void qmv_line_kernel(QmvArgs a) {
     return static_cast<uint32_t>(FULL ? t * kWave + lane : min(t * kWave + lane, Kc - 1));
   };
 
-  // ---- 1. raw x of this thread's staging item(s)
+  // ---- 1. raw x of this thread's staging item(s); a wave whose items all
+  // lie past Kc loads nothing (its threads would only re-read chunk Kc - 1)
   uint32_t raw[XI][16];
 #pragma unroll
   for (int i = 0; i < XI; ++i) {
-    const int it = min(static_cast<int>(threadIdx.x) + i * NT, Kc - 1);
-    load_x_chunk(byte_offset(a.x, static_cast<uint32_t>(it) * 64), raw[i]);
+    if (wid * kWave + i * NT < Kc) {                          // wave-uniform
+      const int it = min(static_cast<int>(threadIdx.x) + i * NT, Kc - 1);
+      load_x_chunk(byte_offset(a.x, static_cast<uint32_t>(it) * 64), raw[i]);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -99,7 +102,7 @@ __global__ __launch_bounds__(WPB * kWave) void qmv_line_kernel(QmvArgs a) {
 #pragma unroll
   for (int i = 0; i < XI; ++i) {
     const int it = static_cast<int>(threadIdx.x) + i * NT;
-    if ((i + 1) * NT <= CPL * kWave || it < Kc) {
+    if (wid * kWave + i * NT < Kc && ((i + 1) * NT <= CPL * kWave || it < Kc)) {
       const int its = min(it, Kc - 1);
       if constexpr (PAIR) stage_pairs_raw<BITS, 1>(raw[i], smem, 0, its);
       else stage_f32_raw<1>(raw[i], smem, 0, its);
