@@ -119,6 +119,23 @@ def test_qmv_ragged_shapes(dev, bits, g, M):
     check_t2(run_qmv(x, dw, ds, db, g, bits, dev, out_f32=True), ref, "f32")
 
 
+@pytest.mark.parametrize("N,K,g", [(4100, 4224, 32), (4100, 4096, 128), (300, 8192, 64),
+                                   (300, 8256, 32), (77, 4160, 64)])
+def test_qmv_two_bit_shapes(dev, N, K, g):
+    """2-bit codes (8-byte chunks) past the tile and step boundaries: more
+    than 4096 rows (two rows per wave) with a ragged lane tail (K = 4224),
+    K = 8192 and 8256 past the straight-line kernel's 4096, and an odd
+    number of groups per row (K = 4160 with 65 groups of 64)."""
+    bits = 2
+    w = crafted_weight(N, K, seed=N + K + g)
+    ow, os_, ob = oracle.quantize_pack(w, g, bits)
+    x = synth.activation_bf16((1, K), seed=3)
+    ref = oracle.qmv(x, ow, os_, ob, g, bits)
+    dw, ds, db = to_dev_u32(ow, dev), to_dev_bf16(os_, dev), to_dev_bf16(ob, dev)
+    check_t1(run_qmv(x, dw, ds, db, g, bits, dev), ref, "bf16")
+    check_t2(run_qmv(x, dw, ds, db, g, bits, dev, out_f32=True), ref, "f32")
+
+
 @pytest.mark.parametrize("bits", BITS)
 @pytest.mark.parametrize("N,K,g", [(1, 32, 32), (3, 64, 64), (17, 128, 128),
                                    (64, 96, 32), (5, 2048, 64)])
@@ -218,7 +235,7 @@ def _ffn_weights(dev, N=14336, K=4096, bits=8, g=64, down=True):
     return mats, on_dev
 
 
-@pytest.mark.parametrize("bits,g", [(8, 64), (4, 64), (3, 32)])
+@pytest.mark.parametrize("bits,g", [(8, 64), (4, 64), (3, 32), (2, 32), (2, 128)])
 def test_gate_up_equals_two_qmv_and_oracle(dev, bits, g):
     N, K = (14336, 4096) if bits == 8 else (2000, 2048)
     (wg, wu), (dg, du) = _ffn_weights(dev, N, K, bits, g, down=False)
