@@ -45,6 +45,20 @@ __global__ __launch_bounds__(WPB * kWave) void qmv_line_kernel(QmvArgs a) {
   const int64_t wstride = static_cast<int64_t>(Kc) * BITS;
   const int64_t gstride = Kc >> a.gshift;
 
+  uint32_t raw[XI][16];
+  if constexpr (RPW == 1) {
+    // x first: one row per wave is used for small matrices, where issuing
+    // x before the row addresses are formed measured faster
+#pragma unroll
+    for (int i = 0; i < XI; ++i) {
+      if (wid * kWave + i * NT < Kc) {                        // wave-uniform
+        const int it = min(static_cast<int>(threadIdx.x) + i * NT, Kc - 1);
+        load_x_chunk(byte_offset(a.x, static_cast<uint32_t>(it) * 64), raw[i]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
   const uint32_t *wrow[RPW];
   const uint16_t *srow[RPW], *brow[RPW];
 #pragma unroll
@@ -62,16 +76,19 @@ __global__ __launch_bounds__(WPB * kWave) void qmv_line_kernel(QmvArgs a) {
   };
 
   // ---- 1. raw x of this thread's staging item(s); a wave whose items all
-  // lie past Kc loads nothing (its threads would only re-read chunk Kc - 1)
-  uint32_t raw[XI][16];
+  // lie past Kc loads nothing (its threads would only re-read chunk Kc - 1).
+  // With one row per wave (small matrices) they were issued above, before
+  // the row addresses are formed.
+  if constexpr (RPW != 1) {
 #pragma unroll
-  for (int i = 0; i < XI; ++i) {
-    if (wid * kWave + i * NT < Kc) {                          // wave-uniform
-      const int it = min(static_cast<int>(threadIdx.x) + i * NT, Kc - 1);
-      load_x_chunk(byte_offset(a.x, static_cast<uint32_t>(it) * 64), raw[i]);
+    for (int i = 0; i < XI; ++i) {
+      if (wid * kWave + i * NT < Kc) {                        // wave-uniform
+        const int it = min(static_cast<int>(threadIdx.x) + i * NT, Kc - 1);
+        load_x_chunk(byte_offset(a.x, static_cast<uint32_t>(it) * 64), raw[i]);
+      }
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
-  __builtin_amdgcn_sched_barrier(0);
 
   // ---- 2. scales and biases of every step
   uint16_t sv[CPL][RPW], bv[CPL][RPW];

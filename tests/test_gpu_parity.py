@@ -222,6 +222,24 @@ def test_qmv_ragged_rows_past_4096(dev, bits, M):
     check_t2(run_qmv(x, dw, ds, db, g, bits, dev, out_f32=True), ref, "f32")
 
 
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("M", (2, 3, 4))
+@pytest.mark.parametrize("N,g", [(1000, 64), (4100, 128)])
+def test_qmv_vectors_partial_second_step(dev, bits, M, N, g):
+    """K = 3968 (124 chunks: a second 64-lane step with 4 lanes idle) at 2-4
+    rows of x, at most 4096 rows (one row per wave) and past it (two rows per
+    wave): the several-vector slab with a partial step, and with 3 of a
+    4-vector slab's slots filled."""
+    K = 3968
+    w = crafted_weight(N, K, seed=bits * 13 + M + g)
+    ow, os_, ob = oracle.quantize_pack(w, g, bits)
+    dw, ds, db = to_dev_u32(ow, dev), to_dev_bf16(os_, dev), to_dev_bf16(ob, dev)
+    x = synth.activation_bf16((M, K), seed=500 + M)
+    ref = oracle.qmv(x, ow, os_, ob, g, bits)
+    check_t1(run_qmv(x, dw, ds, db, g, bits, dev), ref, "bf16")
+    check_t2(run_qmv(x, dw, ds, db, g, bits, dev, out_f32=True), ref, "f32")
+
+
 # ---------------------------------------------------------------- fused FFN
 def _ffn_weights(dev, N=14336, K=4096, bits=8, g=64, down=True):
     wg = packed(N, K, bits, g, seed=synth.SEED_W)
