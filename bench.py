@@ -51,7 +51,7 @@ COMMON_SOURCES = ("qmv_api.hip", "qmv_device.h")
 FAMILY_SOURCES = {
     "qmv": ("qmv_kernels.h", "qmv_line_kernels.h"),
     "qmm": ("qmm_kernels.h", "qvm_kernels.h"),      # matrix cores + slice reduction
-    "ffn": ("qmv_kernels.h",),
+    "ffn": ("qmv_kernels.h", "qmv_line_kernels.h"),   # gate/up runs the line kernel
     "moe": ("qmv_kernels.h", "qmm_kernels.h"),
     "qvm": ("qvm_kernels.h",),
     "pack": ("pack_kernels.h",),

@@ -35,6 +35,15 @@ __global__ __launch_bounds__(WPB * kWave) void qmv_line_kernel(QmvArgs a) {
   constexpr int kStride = chunk_stride_for<BITS, PAIR, 1>();
   constexpr bool TWO = PAIR && two_sums<BITS>();   // X' follows X (PairPlan)
   constexpr int XI = (CPL * kWave + NT - 1) / NT;   // x staging items per thread
+  // 8-bit codes, and 4-bit codes at one row per wave, stage x in 16-byte
+  // pieces (a quarter chunk) taken by consecutive lanes, so each load
+  // instruction reads 1 KB of x: a float, or a 4-bit pair's two values, lie
+  // inside one piece.  (Against whole chunks per lane, MI355X, 3
+  // alternations: 8-bit 14336x4096 g32/64/128 13.4/13.3/13.2 ->
+  // 13.1/13.0/12.8 us, gate/up 24.5 -> 24.0, 4096x4096 4-bit 4.06 -> 3.98;
+  // but 14336x4096 4-bit, two rows per wave, 7.57 -> 7.71.)
+  constexpr bool PIECES = BITS == 8 || (BITS == 4 && RPW == 1);
+  constexpr int XP = (4 * CPL * kWave + NT - 1) / NT;   // pieces per thread
   extern __shared__ __align__(16) unsigned char smem[];
 
   const int Kc = a.K >> 5;
@@ -45,8 +54,23 @@ __global__ __launch_bounds__(WPB * kWave) void qmv_line_kernel(QmvArgs a) {
   const int64_t wstride = static_cast<int64_t>(Kc) * BITS;
   const int64_t gstride = Kc >> a.gshift;
 
-  uint32_t raw[XI][16];
-  if constexpr (RPW == 1) {
+  uint32_t raw[PIECES ? 1 : XI][16];
+  uint4 praw[PIECES ? XP : 1];
+  if constexpr (PIECES) {
+    // piece t + i NT is quarter (t & 3) of chunk (t + i NT) / 4; a wave
+    // whose pieces all lie past Kc loads nothing, lanes past it re-read
+    // chunk Kc - 1.  Issued before the row addresses are formed (measured
+    // faster here for one and two rows per wave).
+#pragma unroll
+    for (int i = 0; i < XP; ++i) {
+      if ((wid * kWave + i * NT) / 4 < Kc) {                  // wave-uniform
+        const int pc = static_cast<int>(threadIdx.x) + i * NT;
+        const int c = min(pc >> 2, Kc - 1);
+        praw[i] = *reinterpret_cast<const uint4 *>(byte_offset(a.x, static_cast<uint32_t>(c * 64 + (pc & 3) * 16)));
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  } else if constexpr (RPW == 1) {
     // x first: one row per wave is used for small matrices, where issuing
     // x before the row addresses are formed measured faster
 #pragma unroll
@@ -79,7 +103,7 @@ __global__ __launch_bounds__(WPB * kWave) void qmv_line_kernel(QmvArgs a) {
   // lie past Kc loads nothing (its threads would only re-read chunk Kc - 1).
   // With one row per wave (small matrices) they were issued above, before
   // the row addresses are formed.
-  if constexpr (RPW != 1) {
+  if constexpr (RPW != 1 && !PIECES) {
 #pragma unroll
     for (int i = 0; i < XI; ++i) {
       if (wid * kWave + i * NT < Kc) {                        // wave-uniform
@@ -116,13 +140,53 @@ __global__ __launch_bounds__(WPB * kWave) void qmv_line_kernel(QmvArgs a) {
   }
 
   // ---- 4. x into LDS (waits for x only), one barrier
+  if constexpr (PIECES) {
 #pragma unroll
-  for (int i = 0; i < XI; ++i) {
-    const int it = static_cast<int>(threadIdx.x) + i * NT;
-    if (wid * kWave + i * NT < Kc && ((i + 1) * NT <= CPL * kWave || it < Kc)) {
-      const int its = min(it, Kc - 1);
-      if constexpr (PAIR) stage_pairs_raw<BITS, 1>(raw[i], smem, 0, its);
-      else stage_f32_raw<1>(raw[i], smem, 0, its);
+    for (int i = 0; i < XP; ++i) {
+      if ((wid * kWave + i * NT) / 4 < Kc) {                  // wave-uniform
+        const int pc = static_cast<int>(threadIdx.x) + i * NT;
+        const int c = min(pc >> 2, Kc - 1), q = pc & 3;
+        const uint4 v = praw[i];
+        // the chunk's sum: this piece's 8 values in order, then the four
+        // pieces' partial sums across the chunk's adjacent lanes
+        float sum;
+        unsigned char *chunk = smem + c * kStride;
+        if constexpr (PAIR) {
+          sum = dot2_bf16(v.x, 0x3F803F80u, 0.0f);
+          sum = dot2_bf16(v.y, 0x3F803F80u, sum);
+          sum = dot2_bf16(v.z, 0x3F803F80u, sum);
+          sum = dot2_bf16(v.w, 0x3F803F80u, sum);
+          // pair j of the piece = (x[j], x[j + 4])
+          *reinterpret_cast<uint4 *>(chunk + q * 16) = make_uint4(__builtin_amdgcn_perm(v.z, v.x, 0x05040100u),
+                                                                  __builtin_amdgcn_perm(v.z, v.x, 0x07060302u),
+                                                                  __builtin_amdgcn_perm(v.w, v.y, 0x05040100u),
+                                                                  __builtin_amdgcn_perm(v.w, v.y, 0x07060302u));
+        } else {
+          const uint32_t r[4] = {v.x, v.y, v.z, v.w};
+          float f[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            f[k] = (k & 1) ? __uint_as_float(r[k >> 1] & 0xFFFF0000u) : __uint_as_float(r[k >> 1] << 16);
+          sum = f[0];
+#pragma unroll
+          for (int k = 1; k < 8; ++k) sum += f[k];
+          *reinterpret_cast<float4 *>(chunk + q * 32) = make_float4(f[0], f[1], f[2], f[3]);
+          *reinterpret_cast<float4 *>(chunk + q * 32 + 16) = make_float4(f[4], f[5], f[6], f[7]);
+        }
+        sum += dpp<kDppXor1>(sum);
+        sum += dpp<kDppXor2>(sum);
+        if (q == 0) *reinterpret_cast<float *>(chunk + vec_bytes<PAIR>()) = sum;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < XI; ++i) {
+      const int it = static_cast<int>(threadIdx.x) + i * NT;
+      if (wid * kWave + i * NT < Kc && ((i + 1) * NT <= CPL * kWave || it < Kc)) {
+        const int its = min(it, Kc - 1);
+        if constexpr (PAIR) stage_pairs_raw<BITS, 1>(raw[i], smem, 0, its);
+        else stage_f32_raw<1>(raw[i], smem, 0, its);
+      }
     }
   }
   __syncthreads();
