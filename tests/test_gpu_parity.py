@@ -223,13 +223,15 @@ def test_qmv_ragged_rows_past_4096(dev, bits, M):
 
 
 @pytest.mark.parametrize("bits", BITS)
-@pytest.mark.parametrize("M", (2, 3, 4))
+@pytest.mark.parametrize("M", (1, 2, 3, 4))
 @pytest.mark.parametrize("N,g", [(1000, 64), (4100, 128)])
 def test_qmv_vectors_partial_second_step(dev, bits, M, N, g):
-    """K = 3968 (124 chunks: a second 64-lane step with 4 lanes idle) at 2-4
+    """K = 3968 (124 chunks: a second 64-lane step with 4 lanes idle) at 1-4
     rows of x, at most 4096 rows (one row per wave) and past it (two rows per
-    wave): the several-vector slab with a partial step, and with 3 of a
-    4-vector slab's slots filled."""
+    wave): the straight-line kernel with a partial step (its x staged in
+    16-byte pieces for 4- and 8-bit codes at one row per wave and for 8-bit
+    codes at two), and the several-vector slab with a partial step and with
+    3 of a 4-vector slab's slots filled."""
     K = 3968
     w = crafted_weight(N, K, seed=bits * 13 + M + g)
     ow, os_, ob = oracle.quantize_pack(w, g, bits)
