@@ -50,7 +50,7 @@ CSRC = os.path.join(ROOT, "bit_affine_quantized_amd", "csrc")
 COMMON_SOURCES = ("qmv_api.hip", "qmv_device.h")
 FAMILY_SOURCES = {
     "qmv": ("qmv_kernels.h", "qmv_line_kernels.h"),
-    "qmm": ("qmm_kernels.h", "qvm_kernels.h"),      # matrix cores + slice reduction
+    "qmm": ("qmm_kernels.h", "qvm_kernels.h", "qmf_kernels.h"),   # matrix cores (split-K or one pass)
     "ffn": ("qmv_kernels.h", "qmv_line_kernels.h"),   # gate/up runs the line kernel
     "moe": ("qmv_kernels.h", "qmm_kernels.h"),
     "qvm": ("qvm_kernels.h",),

@@ -15,7 +15,6 @@ BENCH_LIB = os.path.join(PKG, "libqmv_bench.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["qmv_api.hip"]
-HEADERS = ["qmv_device.h", "qmv_kernels.h", "qmv_line_kernels.h", "pack_kernels.h"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -15,6 +15,7 @@
 #include "qmv_line_kernels.h"
 #include "qvm_kernels.h"
 #include "qmm_kernels.h"
+#include "qmf_kernels.h"
 
 namespace {
 
@@ -615,6 +616,63 @@ int run_qmm(const uint16_t *x, const uint32_t *w_q, const uint16_t *scales, cons
   return ok();
 }
 
+// ------------------------------------------------------------------ qmf
+// From QMV_QMM_MIN_M up to 16 rows of x against a 4-bit weight with K = 2048
+// or 4096: one pass on the matrix cores, K split across the waves of a
+// workgroup (qmf_kernels.h), no partial sums and no second kernel.
+// 4096x4096 g64 on MI355X against the split-K product: M = 5 9.07 -> 6.33
+// us, M = 8 9.11 -> 6.92, M = 16 9.30 -> 8.10 (and at M = 4, 6.36 against
+// 5.87 on the one-slab matvec, which keeps M <= 4).  QMV_QMF=0 in the
+// environment turns it off (read once per process).
+static int qmf_enabled() {
+  static const int v = [] {
+    const char *e = std::getenv("QMV_QMF");
+    return (e && e[0] == '0' && e[1] == '\0') ? 0 : 1;
+  }();
+  return v;
+}
+
+static bool qmf_fits(int64_t M, int64_t N, int64_t K, int bits) {
+  return bits == 4 && M >= 2 && M <= 16 && (K == 2048 || K == 4096) &&
+         N * K / 2 < (int64_t(1) << 32) && M * K * 2 < (int64_t(1) << 32);
+}
+
+template <int CW, int CPG>
+int launch_qmf_t(const qmvk::QmfArgs &a, hipStream_t st) {
+  const int64_t blocks = (a.N + 15) / 16;
+  if (blocks > 0x7FFFFFFF) return fail(QMV_EUNSUPPORTED, "qmv: too many rows");
+  constexpr int lds = qmvk::qmf_lds_bytes<CW>();
+  auto kern = qmvk::qmf_kernel<CW, CPG>;
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(qmvk::kQmfThreads), lds, st, a);
+  return check_launch("qmv (matrix cores, one pass)");
+}
+
+template <int CW>
+int launch_qmf_g(int gshift, const qmvk::QmfArgs &a, hipStream_t st) {
+  switch (gshift) {
+    case 0: return launch_qmf_t<CW, 1>(a, st);
+    case 1: return launch_qmf_t<CW, 2>(a, st);
+    default: return launch_qmf_t<CW, 4>(a, st);
+  }
+}
+
+int run_qmf(const uint16_t *x, const uint32_t *w_q, const uint16_t *scales, const uint16_t *biases, void *y,
+            int64_t M, int64_t N, int64_t K, int group_size, int out_f32, hipStream_t st) {
+  qmvk::QmfArgs a{};
+  a.x = x;
+  a.w = w_q;
+  a.s = scales;
+  a.b = biases;
+  a.y = y;
+  a.N = N;
+  a.y_ld = N;
+  a.K = static_cast<int>(K);
+  a.M = static_cast<int>(M);
+  a.out_f32 = out_f32;
+  const int gshift = gshift_of(group_size);
+  return K == 2048 ? launch_qmf_g<8>(gshift, a, st) : launch_qmf_g<16>(gshift, a, st);
+}
+
 template <int BITS>
 int launch_dequant_t(const uint32_t *w_q, const uint16_t *scales, const uint16_t *biases,
                      int64_t N, int64_t K, int gshift, int out_f32, void *out, hipStream_t st) {
@@ -733,6 +791,11 @@ int qmv_impl(const uint16_t *x, const uint32_t *w_q, const uint16_t *scales, con
   if (ptrs) {
     if (int rc = check_aligned("qmv", x, "x")) return rc;
     if (int rc = check_aligned("qmv", w_q, "w_q")) return rc;
+  }
+  if (M >= qmm_min_m() && qmf_fits(M, N, K, bits) && qmf_enabled()) {
+    if (ws.sizing) return ok();   // no workspace
+    if (int rc = run_qmf(x, w_q, scales, biases, y, M, N, K, group_size, out_dtype == QMV_OUT_F32, st)) return rc;
+    return ok();
   }
   if (M >= qmm_min_m() && N * K * bits / 8 < (int64_t(1) << 32) &&
       N * (K / group_size) * 2 < (int64_t(1) << 32) && 64 * K * 2 < (int64_t(1) << 32)) {

@@ -85,10 +85,14 @@ int qmv_pack(const float *w, int64_t N, int64_t K, int group_size, int bits,
  *                  K must be a multiple of group_size.  Up to 4 rows of x:
  *                  the W stream is read once per slab of up to 4 rows.  With
  *                  5 or more rows the matrix cores are used (64-row slabs of
- *                  x, W read once per slab) and K is split into slices.
- *                  That threshold (5) can be replaced by a positive integer
- *                  in the environment variable QMV_QMM_MIN_M, read once per
- *                  process, to time both paths on one shape.
+ *                  x, W read once per slab) and K is split into slices;
+ *                  for 4-bit codes with K = 2048 or 4096 and at most 16
+ *                  rows, in one pass with no slices (K split across the
+ *                  waves of a workgroup, no workspace).  That threshold (5)
+ *                  can be replaced by a positive integer in the environment
+ *                  variable QMV_QMM_MIN_M, and QMV_QMF=0 turns the one-pass
+ *                  form off (both read once per process), to time the paths
+ *                  on one shape.
  *   transpose = 0: W packed [K, N] (groups along N, quantized.h qvm and its
  *                  split-K variant); y[m, n] = sum_k x[m, k] * w_hat[k, n].
  *                  N must be a multiple of group_size; W is read once per

@@ -160,9 +160,16 @@ def test_workspace_none_for_matvec_slabs(M):
     assert _ws_bytes(M, 14336, 4096) == (q.QMV_OK, 0)
 
 
+@pytest.mark.parametrize("M", (5, 8, 16))
+@pytest.mark.parametrize("K", (2048, 4096))
+def test_workspace_none_for_one_pass_matrix_cores(M, K):
+    """4-bit, K = 2048 or 4096, 5-16 rows of x: one pass, no slices."""
+    assert _ws_bytes(M, 4096, K) == (q.QMV_OK, 0)
+
+
 @pytest.mark.parametrize("M,N,K,transpose", [(1, 4096, 4096, 0), (4, 4096, 4096, 0),
-                                             (8, 4096, 4096, 1), (64, 4096, 4096, 1),
-                                             (300, 1024, 2048, 1)])
+                                             (8, 4096, 8192, 1), (17, 4096, 4096, 1),
+                                             (64, 4096, 4096, 1), (300, 1024, 2048, 1)])
 def test_workspace_split_k_sizes(M, N, K, transpose):
     rc, nbytes = _ws_bytes(M, N, K, transpose=transpose)
     assert rc == q.QMV_OK

@@ -1,8 +1,9 @@
-"""GPU parity of the matrix-core path that qmv (transpose = 1) takes for 5 or
+"""GPU parity of the matrix-core paths that qmv (transpose = 1) takes for 5 or
 more rows of x, against the oracle's exact fp64 product: T1 for bf16 outputs,
 T2 for the fp32 debugging mode.  Covers every bit width and group size,
 partial 64-row W blocks and 8-chunk K blocks, x rows beyond one 64-row slab,
-the split-K and single-slice launches, and run-to-run determinism."""
+the split-K and single-slice launches, the one-pass form (4-bit, K = 2048 or
+4096, up to 16 rows) and run-to-run determinism."""
 import numpy as np
 import pytest
 
@@ -89,3 +90,29 @@ def test_qmm_zero_x_gives_exact_zero(dev):
     dw = _dev(_pack(N, K, g, bits, seed=5), dev)
     x = np.zeros((M, K), dtype=np.uint16)
     np.testing.assert_array_equal(_run(x, dw, g, bits, dev), np.zeros((M, N), np.uint16))
+
+
+@pytest.mark.parametrize("K", (2048, 4096))
+@pytest.mark.parametrize("g", GROUPS)
+@pytest.mark.parametrize("M", (5, 8, 13, 16))
+def test_qmf_one_pass_shapes(dev, K, g, M):
+    """4-bit codes, K = 2048 or 4096, 5-16 rows of x: the one-pass product (K
+    split across the waves of a workgroup, no slices).  N = 1000 is not a
+    multiple of its 16-row tile."""
+    _check(1000, K, g, 4, M, dev, seed=M * 7 + g + K)
+
+
+def test_qmf_one_row_tile_and_repeat(dev):
+    """N = 17: a second tile holding one W row (the others re-read row 16 and
+    are never stored); repeated calls are bit-identical."""
+    N, K, g, bits, M = 17, 4096, 64, 4, 16
+    w = _pack(N, K, g, bits, seed=9)
+    dw = _dev(w, dev)
+    x = synth.activation_bf16((M, K), seed=10)
+    ref = oracle.qmv(x, *w, g, bits)
+    a = _run(x, dw, g, bits, dev, out_f32=True)
+    check_t2(a, ref, "f32")
+    check_t1(_run(x, dw, g, bits, dev), ref, "bf16")
+    for _ in range(3):
+        np.testing.assert_array_equal(_run(x, dw, g, bits, dev, out_f32=True).view(np.uint32),
+                                      a.view(np.uint32))

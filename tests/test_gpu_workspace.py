@@ -32,14 +32,16 @@ def _call(q, c, out_f32, workspace=None):
 
 
 # (M, N, K, transpose): qvm with one and four vectors, a ragged column block
-# (N not a multiple of 512) and many slices (large K); the matrix-core path
-# with one and two 64-row slabs (the second launch reuses the counters) and a
-# ragged row block (N not a multiple of 64)
+# (N not a multiple of 512) and many slices (large K); the split-K
+# matrix-core path with one and two 64-row slabs (the second launch reuses
+# the counters) and a ragged row block (N not a multiple of 64).  (4-bit with
+# K = 2048 or 4096 and at most 16 rows runs in one pass with no workspace:
+# test_one_pass_shapes_need_no_workspace.)
 CASES = [
     (1, 4096, 4096, False), (4, 1024, 4096, False), (2, 4160, 2048, False),
     (1, 512, 16384, False),
-    (8, 4096, 4096, True), (64, 1024, 2048, True), (100, 1000, 1024, True),
-    (5, 2112, 4096, True),
+    (8, 4096, 8192, True), (64, 1024, 2048, True), (100, 1000, 1024, True),
+    (5, 2112, 1024, True),
 ]
 
 
@@ -85,11 +87,28 @@ def test_with_workspace_back_to_back_without_sync(dev):
     import torch
 
     import bit_affine_quantized_amd as q
-    c = _case(dev, 16, 2048, 4096, True, seed=7)
-    nb = q.qmv_workspace_bytes(16, 2048, 4096, 64, 4, True)
+    c = _case(dev, 24, 2048, 4096, True, seed=7)
+    nb = q.qmv_workspace_bytes(24, 2048, 4096, 64, 4, True)
+    assert nb > 0
     ws = torch.empty(nb, dtype=torch.uint8, device=dev)
     want = _call(q, c, False)
     ys = [q.qmv(c["x"], *c["w"], group_size=64, bits=4, workspace=ws) for _ in range(20)]
     torch.cuda.synchronize()
     for i, y in enumerate(ys):
         np.testing.assert_array_equal(bf16_to_np_bits(y), want, err_msg=f"call {i}")
+
+
+@pytest.mark.parametrize("M,N,K", [(5, 4096, 4096), (16, 1000, 2048)])
+def test_one_pass_shapes_need_no_workspace(dev, M, N, K):
+    """4-bit, K = 2048 or 4096, 5-16 rows of x: the one-pass matrix-core
+    product splits K inside a workgroup only, so the workspace size is 0 and
+    qmv_with_workspace runs without one, equal to qmv."""
+    import torch
+
+    import bit_affine_quantized_amd as q
+    c = _case(dev, M, N, K, True, seed=M + K)
+    assert q.qmv_workspace_bytes(M, N, K, 64, 4, True) == 0
+    y1 = _call(q, c, True)
+    y2 = _call(q, c, True, torch.empty(0, dtype=torch.uint8, device=dev))
+    np.testing.assert_array_equal(y1.view(np.uint32), y2.view(np.uint32))
+    check_t2(y1, c["ref"], "f32")

@@ -54,7 +54,7 @@ def test_noalloc_matches_with_workspace_two_calls(dev, transpose, out_f32):
 
     import bit_affine_quantized_amd as q
     big = _case(dev, 64 if transpose else 4, 4096, 4096, transpose, 31)
-    small = _case(dev, 8 if transpose else 2, 1024, 2048, transpose, 32)
+    small = _case(dev, 8 if transpose else 2, 1024, 1024 if transpose else 2048, transpose, 32)
     assert q.qmv_workspace_bytes(big["M"], big["N"], big["K"], 64, 4, transpose) > \
         q.qmv_workspace_bytes(small["M"], small["N"], small["K"], 64, 4, transpose) > 0
     for c in (big, small):
