@@ -501,28 +501,39 @@ def cpu_baseline(wl: Workload, runs: int = 5):
                       "fp64 dequant-and-dot"}
 
 
-def _time_queued(step, steps, stream, info=None):
+def _time_queued(step, steps, stream, info=None, lead_ms=2.0):
     """K eager launches queued behind a bounded device spin, timed by events.
 
-    The spin (a few times the measured host enqueue time of the K steps)
-    holds the stream while the host enqueues the start event, the K steps and
-    the end event, so the timed region holds only the K launches running back
-    to back; neither the host's per-launch cost nor a graph launch falls
-    inside it.  If the host took longer than the spin to enqueue, the queue
-    may have drained and the time is pessimistic; `queue_drained` says so."""
+    The spin (a few times the measured host enqueue time) holds the stream
+    while the host enqueues some untimed lead steps, the start event, the K
+    steps and the end event, so the timed region holds only the K launches
+    running back to back; neither the host's per-launch cost nor a graph
+    launch falls inside it.  The lead steps (at least `lead_ms` of GPU work)
+    run between the spin and the start event, so the timed steps start on a
+    GPU that has been busy with the same work, not idle behind a one-wave
+    spin.  If the host took longer than the spin to enqueue, the queue may
+    have drained and the time is pessimistic; `queue_drained` says so."""
     import torch
     torch.cuda.synchronize()
     probe = min(steps, 20)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
     h0 = time.perf_counter()
+    e0.record(stream)
     for i in range(probe):
         step(i, stream)
+    e1.record(stream)
     host_per_step = (time.perf_counter() - h0) / probe
     torch.cuda.synchronize()
-    spin_ms = min(max(1.0, 3e3 * host_per_step * steps), 3000.0)
+    gpu_per_step = e0.elapsed_time(e1) / probe
+    lead = int(min(max(math.ceil(lead_ms / max(gpu_per_step, 1e-4)), 1), 20000))
+    spin_ms = min(max(1.0, 3e3 * host_per_step * (lead + steps)), 3000.0)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda._sleep(int(spin_ms * _spin_cycles_per_ms()))
     h0 = time.perf_counter()
+    for i in range(lead):
+        step(steps + i, stream)
     t0.record(stream)
     for i in range(steps):
         step(i, stream)
@@ -531,6 +542,7 @@ def _time_queued(step, steps, stream, info=None):
     torch.cuda.synchronize()
     if info is not None:
         info["spin_ms"] = round(spin_ms, 3)
+        info["lead_steps"] = lead
         info["host_enqueue_ms"] = round(enqueue_ms, 3)
         info["queue_drained"] = enqueue_ms > spin_ms
     return t0.elapsed_time(t1) / steps
