@@ -20,27 +20,36 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "qmv_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# The oracle mutation test points this at a deliberately broken copy, built
+# from an edited source, to check that the pins catch the mistake.
+_ALT_LIB = os.environ.get("QMV_ORACLE_LIB")
 
 _lib = None
 
 
+def compile_source(src: str, out: str) -> None:
+    """gcc, no fast-math, no FMA contraction: one IEEE operation per step."""
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared",
+           "-ffp-contract=off", "-fno-fast-math", "-fno-finite-math-only",
+           "-o", tmp, src, "-lm"]
+    subprocess.check_call(cmd)
+    os.replace(tmp, out)
+
+
 def build(force: bool = False) -> str:
-    """Compile the oracle with gcc: no fast-math, no FMA contraction."""
+    """Compile the oracle (the library the package loads)."""
+    if _ALT_LIB:
+        return _ALT_LIB
     if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp%d" % os.getpid()
-        cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared",
-               "-ffp-contract=off", "-fno-fast-math", "-fno-finite-math-only",
-               "-o", tmp, _SRC, "-lm"]
-        subprocess.check_call(cmd)
-        os.replace(tmp, _LIB)
+        compile_source(_SRC, _LIB)
     return _LIB
 
 
 def _load():
     global _lib
     if _lib is None:
-        build()
-        lib = ctypes.CDLL(_LIB)
+        lib = ctypes.CDLL(build())
         P = ctypes.c_void_p
         I64 = ctypes.c_int64
         I = ctypes.c_int
