@@ -16,10 +16,10 @@
 // memory-counter waits): its W in 16-byte pieces, consecutive lanes taking
 // consecutive chunks of one row (every load instruction reads whole cache
 // lines), the scales and biases of its groups, and for every chunk one
-// 16-byte x piece per lane (x rows past M re-read row M - 1; their results
-// are never stored).  W then goes through the wave's own LDS region once to
-// reach the MFMA's row-per-lane layout.  The 8 waves' 16 x 16 results meet
-// in LDS and are added in wave order.
+// 16-byte x piece per lane (lanes of x rows past M read zeros without a
+// memory request; their results are never stored).  W then goes through the
+// wave's own LDS region once to reach the MFMA's row-per-lane layout.  The 8
+// waves' 16 x 16 results meet in LDS and are added in wave order.
 #pragma once
 
 #include "qmm_kernels.h"
@@ -110,15 +110,23 @@ __global__ __launch_bounds__(kQmfThreads) void qmf_kernel(QmfArgs a) {
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  // ---- 3. x: chunk cc's 8 values 8kb..8kb+7 of x row j (rows past M
-  // re-read row M - 1)
+  // ---- 3. x: chunk cc's 8 values 8kb..8kb+7 of x row j, through a buffer
+  // resource over the M rows: lanes of rows past M take an offset past its
+  // end, so their loads return zeros and make no memory request (the A rows
+  // they fill only meet outputs that are never stored), while every lane
+  // still issues the same instructions
   uint4 xv[CW];
   {
-    const int m = j < a.M ? j : a.M - 1;
-    const uint32_t xo = static_cast<uint32_t>(m) * static_cast<uint32_t>(a.K) * 2u +
-                        static_cast<uint32_t>(c0) * 64u + static_cast<uint32_t>(kb) * 16u;
+    const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(a.x), 0, a.M * a.K * 2, kBufferDword3);
+    const uint32_t xo = j < a.M ? static_cast<uint32_t>(j) * static_cast<uint32_t>(a.K) * 2u +
+                                      static_cast<uint32_t>(c0) * 64u + static_cast<uint32_t>(kb) * 16u
+                                : 0x80000000u;
 #pragma unroll
-    for (int cc = 0; cc < CW; ++cc) xv[cc] = *reinterpret_cast<const uint4 *>(byte_offset(a.x, xo + cc * 64u));
+    for (int cc = 0; cc < CW; ++cc) {
+      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(xrs, xo + cc * 64u, 0, 0);
+      xv[cc] = make_uint4(v.x, v.y, v.z, v.w);
+    }
   }
 
   // ---- 4. W through the wave's LDS region: row r, chunk cc at r RB + 16 cc
