@@ -165,8 +165,11 @@ int launch_qmv_t(const qmvk::QmvArgs &a, hipStream_t st) {
     }
   }
   if constexpr (XIN == qmvk::XIN_PLAIN) {
+    // one row per wave; 4-vector slabs in 16-wave workgroups (one per CU at
+    // 4096 rows: 4096x4096 4-bit, 4 rows of x, on MI355X 5.70-5.75 ->
+    // 5.59-5.61 us against 8 waves, 7.3-7.5 with 4)
     if (static_cast<int64_t>(a.nmat) * a.N <= QMV_SMALL_ROWS && !QMV_FORCE_WPB)
-      return launch_qmv_wpb<BITS, MV, XIN, 8, 1>(a, lds, st);
+      return launch_qmv_wpb<BITS, MV, XIN, (MV == 4 ? 16 : 8), 1>(a, lds, st);
   }
   if (qmv_waves_per_block(lds) == 4) return launch_qmv_wpb<BITS, MV, XIN, 4>(a, lds, st);
   return launch_qmv_wpb<BITS, MV, XIN, 8>(a, lds, st);
